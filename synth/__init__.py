@@ -1,0 +1,133 @@
+"""Seeded synthetic inputs for the NVFP4 W4A16 matmul (numpy, CPU).
+
+This module is the only thing the CPU oracle (``oracle/``) and the HIP library
+(``block_scaled_fp4_w4a16_amd``) have in common: tests and the benchmark draw
+inputs here and hand the same bytes to both.  It imports neither of them and
+contains none of their arithmetic (no decoding, no matmul); it draws random
+numbers and writes them in the checkpoint's storage format.
+
+Workload recipe (shapes from the FlashRT page "Qwen3.6-27B NVFP4 on RTX 5090",
+section 1: hidden size 5120; MLP width 17408 and the head width 248320 are the
+synthetic shapes of the benchmark configurations):
+  * weights  W ~ N(0, 0.02) fp32 from ``numpy.random.default_rng(seed)``,
+    stored as NVFP4: E2M1 codes two per byte (low nibble = even input), one
+    E4M3 scale per 16 inputs along K, fp32 global scale g = 448/amax;
+  * activations x ~ N(0, 1) rounded to bf16 (round to nearest even);
+  * "SwiGLU-shaped" activations for the down projection: bf16(a*sigmoid(a)*b)
+    with a, b ~ N(0, 1) independent (a heavy-tailed distribution).
+
+Storage encoding used for the weights (the pages give only the schema; this
+recipe is the plainest one consistent with g = 448/amax): per 16-block the
+scale is the E4M3 value nearest to blockmax*g/6 (ties to even, saturating at
+448); each weight's code is the E2M1 value nearest to W*g/scale (ties to the
+even code, saturating at 6, sign kept); a block whose scale is 0 gets code 0.
+The E4M3 value table comes from torch's float8_e4m3fn type; the E2M1 grid is
+the OCP MX element table {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+SIGMA_W = 0.02
+
+# E2M1 magnitudes by code 0..7 (OCP Microscaling spec, FP4 E2M1 element table)
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+_E4M3_TABLE = None  # values of codes 0x00..0x7E, from torch's float8_e4m3fn
+
+
+def _e4m3_table() -> np.ndarray:
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        import torch
+        codes = torch.arange(0, 0x7F, dtype=torch.uint8)
+        _E4M3_TABLE = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy().copy()
+    return _E4M3_TABLE
+
+
+def _nearest_even(t: np.ndarray, grid: np.ndarray) -> np.ndarray:
+    """Index of the grid value nearest to t >= 0 (grid increasing, starting at 0),
+    ties to the even index, values past the end saturate to the last index."""
+    hi = np.searchsorted(grid, t, side="left")          # first grid value >= t
+    hi = np.minimum(hi, grid.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = t - grid[lo]
+    dhi = grid[hi] - t
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    idx = np.where(pick_hi, hi, lo)
+    idx = np.where(t >= grid[-1], grid.size - 1, idx)
+    return idx.astype(np.int64)
+
+
+def encode_nvfp4(w: np.ndarray):
+    """Store fp32 W [N][K] in the NVFP4 schema: (wq u8 [N][K/2], ws u8 [N][K/16], g fp32)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    if K % 16:
+        raise ValueError("K must be a multiple of 16")
+    aw = np.abs(w)
+    amax = float(aw.max()) if w.size else 0.0
+    g = np.float32(448.0 / amax) if amax > 0 else np.float32(1.0)
+    gd = np.float64(g)
+    bmax = aw.reshape(N, K // 16, 16).max(axis=2).astype(np.float64)
+    del aw
+    tab = _e4m3_table()
+    t = bmax * gd / 6.0
+    sc = _nearest_even(np.minimum(t, 448.0), tab).astype(np.uint8)
+    sc[t <= 0] = 0
+    S = tab[sc.astype(np.int64)]                             # [N][K/16] fp64
+    codes = np.zeros((N, K), dtype=np.uint8)
+    nz = np.repeat(S > 0, 16, axis=1)
+    v = w.astype(np.float64) * gd / np.repeat(np.where(S > 0, S, 1.0), 16, axis=1)
+    mag = _nearest_even(np.abs(v), _E2M1_GRID).astype(np.uint8)
+    sign = np.signbit(v).astype(np.uint8) << 3
+    codes = np.where(nz, sign | mag, 0).astype(np.uint8)
+    wq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    return np.ascontiguousarray(wq), np.ascontiguousarray(sc), np.float32(g)
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def weights_f32(seed: int, N: int, K: int, sigma: float = SIGMA_W) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((N, K), dtype=np.float32) * np.float32(sigma)
+
+
+def nvfp4_weights(seed: int, N: int, K: int, sigma: float = SIGMA_W):
+    """Seeded N(0, sigma) weights stored as NVFP4: (wq, ws, g)."""
+    return encode_nvfp4(weights_f32(seed, N, K, sigma))
+
+
+def activations(seed: int, M: int, K: int) -> np.ndarray:
+    """x ~ N(0, 1) as bf16 bits [M][K]."""
+    rng = np.random.default_rng(seed)
+    return bf16_bits(rng.standard_normal((M, K), dtype=np.float32))
+
+
+def swiglu_activations(seed_a: int, seed_b: int, M: int, K: int) -> np.ndarray:
+    """Heavy-tailed activations bf16(a*sigmoid(a)*b), a, b ~ N(0,1) iid, as bf16 bits."""
+    a = np.random.default_rng(seed_a).standard_normal((M, K)).astype(np.float64)
+    b = np.random.default_rng(seed_b).standard_normal((M, K)).astype(np.float64)
+    return bf16_bits((a * b / (1.0 + np.exp(-a))).astype(np.float32))
+
+
+def random_bytes(seed: int, shape) -> np.ndarray:
+    """Uniform random bytes (any byte pattern is a legal code/scale input)."""
+    return np.random.default_rng(seed).integers(0, 256, size=shape, dtype=np.uint8)
+
+
+# Benchmark configurations: name -> dict(K, N, Ms, seeds, copies)
+CONFIGS = {
+    "tiny": dict(K=256, N=512, Ms=(1,), seed_w=11, seed_x=12, copies=1),
+    "square": dict(K=5120, N=5120, Ms=(1,), seed_w=21, seed_x=22, copies=64),
+    "gate_up": dict(K=5120, N=17408, Ms=(1, 7), seed_gate=31, seed_up=32, seed_x=33, copies=32),
+    "down": dict(K=17408, N=5120, Ms=(1, 2, 4, 7, 8), seed_w=41, seed_a=42, seed_b=43, copies=32),
+}
