@@ -1,0 +1,229 @@
+"""Benchmark: NVFP4 W4A16 matmul on one MI355X.
+
+Default workload (one JSON line on stdout): the square projection, K = N =
+5120, M = 1, with 64 byte-identical NVFP4 weight copies (943.7 MB, past the
+256 MB Infinity Cache) cycled call after call.  One step = one pass over the
+64 copies (64 calls).  Metric: effective weight GB/s = (N*K/2 codes + N*K/16
+scales + 4 B g) per call / time per call, plus % of the 8 TB/s HBM peak.
+
+`--extra` also times the fused gate/up (M = 1, 7) and down (M = 1, 2, 4, 7,
+8) configurations and reports them under "extra" in the same line.
+
+The timed region brackets the calls with HIP events recorded on the stream
+the kernels run on; inputs are resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def weight_bytes(N, K):
+    return N * K // 2 + N * K // 16 + 4
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev_u8(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def to_dev_bf16(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def replicate(t, copies):
+    """`copies` byte-identical replicas in distinct allocations."""
+    return [t.clone() for _ in range(copies)]
+
+
+def time_calls(fns, cycles, warmup_cycles, stream):
+    """Run every fn in `fns` once per cycle; return seconds per call (events)."""
+    import torch
+    for _ in range(warmup_cycles):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(cycles):
+        for f in fns:
+            f()
+    end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / (cycles * len(fns))
+
+
+def bench_square(args, dev, stream):
+    import torch
+    import block_scaled_fp4_w4a16_amd as w4
+    import synth
+    c = synth.CONFIGS["square"]
+    N, K, copies = c["N"], c["K"], c["copies"]
+    log(f"[bench] generating square K={K} N={N} x{copies} copies")
+    wq, ws, g = synth.nvfp4_weights(c["seed_w"], N, K)
+    x = to_dev_bf16(synth.activations(c["seed_x"], 1, K), dev)
+    wqs = replicate(to_dev_u8(wq, dev), copies)
+    wss = replicate(to_dev_u8(ws, dev), copies)
+    gs = replicate(torch.tensor([g], dtype=torch.float32, device=dev), copies)
+    y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+    fns = [lambda i=i: w4.gemm(wqs[i], wss[i], gs[i], x, y=y, stream=stream) for i in range(copies)]
+    torch.cuda.synchronize()
+    # warmup steps, then exactly `steps` steps timed
+    for _ in range(args.warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        for f in fns:
+            f()
+    end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    calls = args.steps * copies
+    per_call = ms * 1e-3 / calls
+    bpc = weight_bytes(N, K)
+    return dict(N=N, K=K, copies=copies, calls=calls, ms=ms, wall=wall, per_call=per_call,
+                bytes_per_call=bpc, gbs=bpc / per_call / 1e9)
+
+
+def bench_extra(dev, stream, cycles=10):
+    import torch
+    import block_scaled_fp4_w4a16_amd as w4
+    import synth
+    out = {}
+    c = synth.CONFIGS["gate_up"]
+    N, K, copies = c["N"], c["K"], c["copies"]
+    log(f"[bench] generating gate_up K={K} N={N} x{copies}")
+    wg = synth.nvfp4_weights(c["seed_gate"], N, K)
+    wu = synth.nvfp4_weights(c["seed_up"], N, K)
+    G = [replicate(to_dev_u8(wg[0], dev), copies), replicate(to_dev_u8(wg[1], dev), copies),
+         replicate(torch.tensor([wg[2]], device=dev), copies)]
+    U = [replicate(to_dev_u8(wu[0], dev), copies), replicate(to_dev_u8(wu[1], dev), copies),
+         replicate(torch.tensor([wu[2]], device=dev), copies)]
+    for M in c["Ms"]:
+        x = to_dev_bf16(synth.activations(c["seed_x"], M, K), dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        work = torch.empty(max(1, w4.workspace_size_gate_up(M, N, K)), dtype=torch.uint8, device=dev)
+        fns = [lambda i=i: w4.gemm_gate_up_swiglu(G[0][i], G[1][i], G[2][i], U[0][i], U[1][i],
+                                                  U[2][i], x, y=y, workspace=work, stream=stream)
+               for i in range(copies)]
+        t = time_calls(fns, cycles, 1, stream)
+        b = 2 * weight_bytes(N, K)
+        out[f"gate_up_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
+        log(f"[bench] gate_up M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
+    del G, U
+    c = synth.CONFIGS["down"]
+    N, K, copies = c["N"], c["K"], c["copies"]
+    log(f"[bench] generating down K={K} N={N} x{copies}")
+    wd = synth.nvfp4_weights(c["seed_w"], N, K)
+    D = [replicate(to_dev_u8(wd[0], dev), copies), replicate(to_dev_u8(wd[1], dev), copies),
+         replicate(torch.tensor([wd[2]], device=dev), copies)]
+    for M in c["Ms"]:
+        x = to_dev_bf16(synth.swiglu_activations(c["seed_a"], c["seed_b"], M, K), dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        work = torch.empty(max(1, w4.workspace_size(M, N, K)), dtype=torch.uint8, device=dev)
+        fns = [lambda i=i: w4.gemm(D[0][i], D[1][i], D[2][i], x, y=y, workspace=work, stream=stream)
+               for i in range(copies)]
+        t = time_calls(fns, cycles, 1, stream)
+        b = weight_bytes(N, K)
+        out[f"down_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
+        log(f"[bench] down M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
+    return out
+
+
+def cpu_baseline(seconds_target=12.0):
+    """The CPU oracle timed on a bounded sample of the square workload."""
+    import oracle
+    import synth
+    c = synth.CONFIGS["square"]
+    N, K = c["N"], c["K"]
+    wq, ws, g = synth.nvfp4_weights(c["seed_w"], N, K)
+    x = synth.activations(c["seed_x"], 1, K)
+    threads = oracle.max_threads()
+    t0 = time.perf_counter()
+    oracle.gemm(wq, ws, g, x, 1, N, K, nthreads=threads)
+    one = time.perf_counter() - t0
+    reps = max(1, min(64, int(seconds_target / max(one, 1e-3))))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.gemm(wq, ws, g, x, 1, N, K, nthreads=threads)
+    dt = (time.perf_counter() - t0) / reps
+    return dict(value=weight_bytes(N, K) / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{reps} calls of the square GEMV (M=1, K=N=5120) by the fp64 C oracle "
+                       f"with {threads} OpenMP threads; {dt*1e3:.1f} ms/call")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--extra", action="store_true", help="also time the gate/up and down configs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_scaled_fp4_w4a16_amd as w4
+    w4.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    r = bench_square(args, dev, stream)
+    log(f"[bench] square: {r['per_call']*1e6:.3f} us/call, {r['gbs']:.1f} GB/s")
+    extra = bench_extra(dev, stream) if args.extra else None
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": "effective weight GB/s (NVFP4 codes + E4M3 scales + g per call / time per call), W4A16 GEMV",
+        "value": round(r["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"] / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4(e2m1+e4m3) x bf16 -> fp32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights NVFP4-encoded, N(0,1) bf16 activations)",
+        "config": {"workload": "square projection GEMV, K=5120 N=5120 M=1, 64 byte-identical "
+                               "weight copies (943.7 MB) cycled per call",
+                   "K": r["K"], "N": r["N"], "M": 1, "copies": r["copies"], "calls_timed": r["calls"],
+                   "us_per_call": round(r["per_call"] * 1e6, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    if extra is not None:
+        line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,183 @@
+"""NVFP4 (block-scaled FP4) weight-only matmul for MI355X: Python binding.
+
+Thin ctypes layer over ``libw4a16.so`` (hand-written HIP kernels for gfx950,
+C ABI declared in ``include/w4a16.h``).  This module only checks tensor
+metadata, allocates outputs with torch and passes raw device pointers and the
+current HIP stream to the library: every arithmetic step runs in the library's
+kernels.  There is no fallback: if the library is not built, importing the
+functions raises.
+
+Weight layout (FlashRT, "Qwen3.6-27B NVFP4 on RTX 5090", section 1 "Model
+dependencies"): ``wq`` uint8 [N, K/2] packed E2M1 codes (low nibble = even
+input), ``ws`` uint8 [N, K/16] E4M3 block scales, ``g`` float32 [1] global
+scale; W = e2m1 * e4m3 / g.  Activations ``x`` are bfloat16 [M, K].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["gemm", "gemm_gate_up_swiglu", "dequant", "workspace_size",
+           "workspace_size_gate_up", "W4A16Error", "library_path", "lib", "MAX_M"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libw4a16.so")
+_lib = None
+MAX_M = 16
+
+OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded libw4a16.so (ctypes); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m block_scaled_fp4_w4a16_amd.build`"
+                          " (hipcc, gfx950). There is no non-HIP fallback.")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.w4a16_gemm.argtypes = [P, P, P, P, P, I, I, I, P, Z, P]
+    L.w4a16_gemm.restype = I
+    L.w4a16_gemm_gate_up_swiglu.argtypes = [P, P, P, P, P, P, P, P, I, I, I, P, Z, P]
+    L.w4a16_gemm_gate_up_swiglu.restype = I
+    L.w4a16_dequant.argtypes = [P, P, P, P, I, I, P]
+    L.w4a16_dequant.restype = I
+    L.w4a16_workspace_size.argtypes = [I, I, I]
+    L.w4a16_workspace_size.restype = Z
+    L.w4a16_workspace_size_gate_up.argtypes = [I, I, I]
+    L.w4a16_workspace_size_gate_up.restype = Z
+    L.w4a16_status_string.argtypes = [I]
+    L.w4a16_status_string.restype = ctypes.c_char_p
+    L.w4a16_abi_version.argtypes = []
+    L.w4a16_abi_version.restype = I
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().w4a16_status_string(int(status)).decode()
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtype, ndim):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def workspace_size(M: int, N: int, K: int) -> int:
+    return int(lib().w4a16_workspace_size(M, N, K))
+
+
+def workspace_size_gate_up(M: int, N: int, K: int) -> int:
+    return int(lib().w4a16_workspace_size_gate_up(M, N, K))
+
+
+def _weights(wq, ws, g, name):
+    _check(wq, f"{name}wq", torch.uint8, 2)
+    _check(ws, f"{name}ws", torch.uint8, 2)
+    _check(g, f"{name}g", torch.float32, None)
+    N, K = wq.shape[0], wq.shape[1] * 2
+    if tuple(ws.shape) != (N, K // 16) or g.numel() != 1:
+        raise ValueError(f"{name}weights: wq {tuple(wq.shape)}, ws {tuple(ws.shape)}, g {tuple(g.shape)} "
+                         "do not form an NVFP4 tensor")
+    return N, K
+
+
+def _workspace(workspace, need, device):
+    if need == 0:
+        return workspace, (workspace.numel() * workspace.element_size() if workspace is not None else 0)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _check(workspace, "workspace", workspace.dtype, None)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def gemm(wq, ws, g, x, y=None, workspace=None, stream=None):
+    """y[M, N] = bf16(x[M, K] @ W^T) with W the NVFP4 tensor (wq, ws, g)."""
+    N, K = _weights(wq, ws, g, "")
+    _check(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError(f"x has K={x.shape[1]}, weights have K={K}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be ({M}, {N})")
+    workspace, wbytes = _workspace(workspace, workspace_size(M, N, K) if M <= MAX_M else 0, x.device)
+    st = lib().w4a16_gemm(_ptr(wq), _ptr(ws), _ptr(g), _ptr(x), _ptr(y), M, N, K,
+                          _ptr(workspace), wbytes, _stream(stream))
+    if st != OK:
+        raise W4A16Error(st, "w4a16_gemm")
+    return y
+
+
+def gemm_gate_up_swiglu(wq_gate, ws_gate, g_gate, wq_up, ws_up, g_up, x, y=None,
+                        workspace=None, stream=None):
+    """y[M, N] = bf16(silu(x @ Wg^T) * (x @ Wu^T)), x read once."""
+    N, K = _weights(wq_gate, ws_gate, g_gate, "gate ")
+    N2, K2 = _weights(wq_up, ws_up, g_up, "up ")
+    if (N, K) != (N2, K2):
+        raise ValueError("gate and up weights must have the same shape")
+    _check(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError(f"x has K={x.shape[1]}, weights have K={K}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be ({M}, {N})")
+    workspace, wbytes = _workspace(workspace, workspace_size_gate_up(M, N, K) if M <= MAX_M else 0,
+                                   x.device)
+    st = lib().w4a16_gemm_gate_up_swiglu(_ptr(wq_gate), _ptr(ws_gate), _ptr(g_gate), _ptr(wq_up),
+                                         _ptr(ws_up), _ptr(g_up), _ptr(x), _ptr(y), M, N, K,
+                                         _ptr(workspace), wbytes, _stream(stream))
+    if st != OK:
+        raise W4A16Error(st, "w4a16_gemm_gate_up_swiglu")
+    return y
+
+
+def dequant(wq, ws, g, w=None, stream=None):
+    """w[N, K] float32 = e2m1 * e4m3 / g (bit-exact)."""
+    N, K = _weights(wq, ws, g, "")
+    if w is None:
+        w = torch.empty((N, K), dtype=torch.float32, device=wq.device)
+    _check(w, "w", torch.float32, 2)
+    if tuple(w.shape) != (N, K):
+        raise ValueError(f"w must be ({N}, {K})")
+    st = lib().w4a16_dequant(_ptr(wq), _ptr(ws), _ptr(g), _ptr(w), N, K, _stream(stream))
+    if st != OK:
+        raise W4A16Error(st, "w4a16_dequant")
+    return w

@@ -1,0 +1,52 @@
+"""Build libw4a16.so (hand-written HIP for gfx950) in-tree with hipcc.
+
+Usage: python -m block_scaled_fp4_w4a16_amd.build
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "w4a16.hip")
+LIB = os.path.join(PKG, "libw4a16.so")
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libw4a16.so)")
+
+
+def build_command(out: str, extra=()) -> list:
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
+        # no packed-fp32 VALU instructions (v_pk_fma_f32 and friends)
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+        *extra, "-o", out, SRC,
+    ]
+
+
+def build(extra=(), out: str = LIB, verbose: bool = False) -> str:
+    tmp = out + ".tmp"
+    cmd = build_command(tmp, extra)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed ({res.returncode}) building {out}")
+    if verbose:
+        err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
+        if err.strip():
+            sys.stderr.write(err + "\n")
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

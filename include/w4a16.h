@@ -1,0 +1,123 @@
+/*
+ * w4a16.h -- C ABI of libw4a16.so: NVFP4 weight-only (W4A16) matmul for
+ * MI355X (gfx950).
+ *
+ * Weight format (FlashRT, "Qwen3.6-27B NVFP4 on RTX 5090", section 1 "Model
+ * dependencies": the compressed-tensors nvfp4-pack-quantized schema):
+ *   wq  uint8  [N][K/2]   FP4 E2M1 codes, two per byte.  Byte j of a row
+ *                         holds input 2j in its low nibble and input 2j+1 in
+ *                         its high nibble (the page says only "two per byte";
+ *                         this order is the library's reading).
+ *   ws  uint8  [N][K/16]  E4M3 (FN variant: max 448, 0x7F/0xFF NaN) scale of
+ *                         the 16 consecutive inputs 16b..16b+15 of the row.
+ *   g   fp32   scalar     per-tensor global scale (448 / amax at quantisation).
+ *   Element value: W[n][k] = e2m1(code) * e4m3(scale) / g.
+ * Activations are bf16 ("A16" of the format name W4A16), passed as their
+ * 16-bit patterns (uint16_t).  All arrays are dense and row-major.
+ *
+ * Shapes: N = out_features, K = in_features (the reduction), M = number of
+ * activation rows (tokens): M = 1 is single-token decode, M up to 16 covers a
+ * speculative verify block (e.g. 6 drafts + 1).
+ *
+ * Ownership: every pointer is device memory owned by the caller (any
+ * allocator).  The library allocates nothing, frees nothing and keeps no
+ * pointer after a call returns.  g is read on the device (no host sync).
+ *
+ * Semantics: every compute call only enqueues work on `stream` (0 = the
+ * default stream) and returns; it never synchronises.  Results for a given
+ * input are bitwise identical from run to run.  Calls are re-entrant; two
+ * calls that share a workspace must not run concurrently.
+ *
+ * Errors: a call that returns anything but W4A16_OK has enqueued nothing,
+ * except W4A16_ERR_LAUNCH, which reports the HIP launch error.  The library
+ * never aborts and never prints.  Unsupported shapes are rejected, not run on
+ * a slower path.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A16_OK = 0,
+  /* null pointer, M/N/K <= 0, or workspace smaller than required */
+  W4A16_ERR_INVALID_VALUE = 1,
+  /* M > 16, K % 256 != 0, a pointer not aligned as documented, or a shape
+   * too large for the kernels (N, K * 2 must fit in 31 bits) */
+  W4A16_ERR_UNSUPPORTED = 2,
+  /* the HIP launch failed (hipGetLastError after the launch) */
+  W4A16_ERR_LAUNCH = 3
+} w4a16_status_t;
+
+/* Largest M (activation rows) the matmul entry points accept. */
+#define W4A16_MAX_M 16
+
+/*
+ * y[M][N] = bf16( x[M][K] * W^T ),  W dequantised from (wq, ws, g) as above,
+ * accumulated in fp32, rounded once to bf16 (nearest even).
+ *   wq, ws, x : 16-byte aligned;  g : 4-byte aligned;  y : 4-byte aligned.
+ *   K % 256 == 0 (keeps every scale row 16-byte aligned).  1 <= M <= 16.
+ *   workspace : device scratch of at least w4a16_workspace_size(M, N, K)
+ *               bytes, 16-byte aligned (may be NULL when that size is 0).
+ *               When the x slice a workgroup needs does not fit in LDS
+ *               (M * K large) or N is small, the reduction is split over K:
+ *               each K-slice writes fp32 partial sums here and a second
+ *               kernel adds them in a fixed order.  Its contents need no
+ *               initialisation and are garbage after the call.
+ * Accuracy contract: |y - y_exact| <= 1e-2 * sum_k |x[m][k] * W[n][k]| + 1e-6
+ * for every (m, n).  Defined by the page's schema and "NVFP4 W4A16" format
+ * (FlashRT, "Qwen3.6-27B NVFP4 on RTX 5090", section 1).
+ */
+w4a16_status_t w4a16_gemm(const uint8_t* wq, const uint8_t* ws, const float* g,
+                          const uint16_t* x, uint16_t* y, int M, int N, int K,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Fused MLP input projections with SwiGLU:
+ *   a = x * Wg^T,  b = x * Wu^T  (both fp32, each with its own g),
+ *   y[M][N] = bf16( silu(a) * b ),  silu(a) = a / (1 + exp(-a)).
+ * x is read once for both matrices; gate and up are separate tensors (no
+ * concatenated copy is needed).  Same alignment, shape and workspace rules as
+ * w4a16_gemm; workspace size from w4a16_workspace_size_gate_up(M, N, K).
+ * The gate/up fusion and a SwiGLU kernel appear on the FlashRT page
+ * (section 4, MLP gate/up fusion) and the qwen36-fp4 README (kernel list).
+ */
+w4a16_status_t w4a16_gemm_gate_up_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,
+                                         const float* g_gate, const uint8_t* wq_up,
+                                         const uint8_t* ws_up, const float* g_up,
+                                         const uint16_t* x, uint16_t* y, int M, int N, int K,
+                                         void* workspace, size_t workspace_bytes,
+                                         hipStream_t stream);
+
+/*
+ * Dequantise to fp32: w[N][K] = e2m1 * e4m3 / g, the product exact and the
+ * division IEEE fp32 (correctly rounded), so the result is bit-exact for
+ * every finite value; a NaN scale gives NaN.  wq, ws : 16-byte aligned;
+ * w : 16-byte aligned; K % 256 == 0.  For tests and debugging.
+ */
+w4a16_status_t w4a16_dequant(const uint8_t* wq, const uint8_t* ws, const float* g, float* w,
+                             int N, int K, hipStream_t stream);
+
+/* Bytes of workspace w4a16_gemm needs for this shape (0 = none). */
+size_t w4a16_workspace_size(int M, int N, int K);
+
+/* Bytes of workspace w4a16_gemm_gate_up_swiglu needs for this shape. */
+size_t w4a16_workspace_size_gate_up(int M, int N, int K);
+
+/* Static English name of a status code (never NULL). */
+const char* w4a16_status_string(w4a16_status_t status);
+
+/* ABI version of this header: bumped on any incompatible change. */
+#define W4A16_ABI_VERSION 1
+int w4a16_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* W4A16_H */

@@ -30,8 +30,6 @@ import numpy as np
 
 SIGMA_W = 0.02
 
-# E2M1 magnitudes by code 0..7 (OCP Microscaling spec, FP4 E2M1 element table)
-_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
 _E4M3_TABLE = None  # values of codes 0x00..0x7E, from torch's float8_e4m3fn
 
 
@@ -58,31 +56,49 @@ def _nearest_even(t: np.ndarray, grid: np.ndarray) -> np.ndarray:
     return idx.astype(np.int64)
 
 
-def encode_nvfp4(w: np.ndarray):
+# Decision thresholds between neighbouring E2M1 magnitudes {0, .5, 1, 1.5, 2, 3, 4, 6}:
+# a magnitude t passes threshold i (moves up one code) when t > mid, or t >= mid
+# where the tie goes to the upper (even) code.  Passing all 7 saturates at 6.
+_E2M1_MIDS_UP_ON_TIE = (0.75, 1.75, 3.5)     # upper code 2, 4, 6 is even
+_E2M1_MIDS_DOWN_ON_TIE = (0.25, 1.25, 2.5, 5.0)  # upper code 1, 3, 5, 7 is odd
+
+
+def _e2m1_code_magnitude(t: np.ndarray) -> np.ndarray:
+    c = np.zeros(t.shape, dtype=np.uint8)
+    for m in _E2M1_MIDS_DOWN_ON_TIE:
+        c += t > m
+    for m in _E2M1_MIDS_UP_ON_TIE:
+        c += t >= m
+    return c
+
+
+def encode_nvfp4(w: np.ndarray, rows_per_chunk: int = 1024):
     """Store fp32 W [N][K] in the NVFP4 schema: (wq u8 [N][K/2], ws u8 [N][K/16], g fp32)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     N, K = w.shape
     if K % 16:
         raise ValueError("K must be a multiple of 16")
-    aw = np.abs(w)
-    amax = float(aw.max()) if w.size else 0.0
+    amax = float(np.abs(w).max()) if w.size else 0.0
     g = np.float32(448.0 / amax) if amax > 0 else np.float32(1.0)
     gd = np.float64(g)
-    bmax = aw.reshape(N, K // 16, 16).max(axis=2).astype(np.float64)
-    del aw
     tab = _e4m3_table()
-    t = bmax * gd / 6.0
-    sc = _nearest_even(np.minimum(t, 448.0), tab).astype(np.uint8)
-    sc[t <= 0] = 0
-    S = tab[sc.astype(np.int64)]                             # [N][K/16] fp64
-    codes = np.zeros((N, K), dtype=np.uint8)
-    nz = np.repeat(S > 0, 16, axis=1)
-    v = w.astype(np.float64) * gd / np.repeat(np.where(S > 0, S, 1.0), 16, axis=1)
-    mag = _nearest_even(np.abs(v), _E2M1_GRID).astype(np.uint8)
-    sign = np.signbit(v).astype(np.uint8) << 3
-    codes = np.where(nz, sign | mag, 0).astype(np.uint8)
-    wq = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return np.ascontiguousarray(wq), np.ascontiguousarray(sc), np.float32(g)
+    wq = np.empty((N, K // 2), dtype=np.uint8)
+    ws = np.empty((N, K // 16), dtype=np.uint8)
+    for r0 in range(0, N, rows_per_chunk):
+        r1 = min(N, r0 + rows_per_chunk)
+        wc = w[r0:r1].astype(np.float64)                         # [n][K]
+        bmax = np.abs(wc).reshape(r1 - r0, K // 16, 16).max(axis=2)
+        t = bmax * gd / 6.0
+        sc = _nearest_even(np.minimum(t, 448.0), tab).astype(np.uint8)
+        sc[t <= 0] = 0
+        ws[r0:r1] = sc
+        S = tab[sc.astype(np.int64)]
+        v = (wc * gd).reshape(r1 - r0, K // 16, 16) / np.where(S > 0, S, 1.0)[:, :, None]
+        codes = _e2m1_code_magnitude(np.abs(v)) | (np.signbit(v).astype(np.uint8) << 3)
+        codes[S <= 0] = 0
+        codes = codes.reshape(r1 - r0, K)
+        wq[r0:r1] = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    return wq, ws, np.float32(g)
 
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:

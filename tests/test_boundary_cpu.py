@@ -1,0 +1,121 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/w4a16.h declares, and its argument checks reject bad calls with the
+documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp4_w4a16_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(w4a16_[a-z0-9_]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(w4.library_path()):
+        from block_scaled_fp4_w4a16_amd import build
+        build.build()
+    return w4.lib()
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for n in ("w4a16_gemm", "w4a16_gemm_gate_up_swiglu", "w4a16_dequant", "w4a16_workspace_size",
+              "w4a16_workspace_size_gate_up", "w4a16_status_string", "w4a16_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(w4.library_path())
+    for n in declared_functions():
+        assert hasattr(raw, n), f"{n} declared in w4a16.h but not exported"
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.w4a16_abi_version() == 1
+    for st in (0, 1, 2, 3):
+        assert len(w4.status_string(st)) > 0
+    assert w4.status_string(99) == "unknown status"
+
+
+P = 0x10000  # a fake, 16-byte aligned "device" address: never dereferenced on these paths
+
+
+def call_gemm(lib, wq=P, ws=P, g=P, x=P, y=P, M=1, N=64, K=256, work=0, wbytes=0):
+    return lib.w4a16_gemm(wq, ws, g, x, y, M, N, K, work, wbytes, None)
+
+
+def call_fused(lib, wq=P, ws=P, g=P, x=P, y=P, M=1, N=64, K=256, work=0, wbytes=0):
+    return lib.w4a16_gemm_gate_up_swiglu(wq, ws, g, wq, ws, g, x, y, M, N, K, work, wbytes, None)
+
+
+@pytest.mark.parametrize("call", [call_gemm, call_fused])
+def test_null_pointers_rejected(lib, call):
+    for arg in ("wq", "ws", "g", "x", "y"):
+        assert call(lib, **{arg: 0}) == w4.ERR_INVALID_VALUE, arg
+
+
+@pytest.mark.parametrize("call", [call_gemm, call_fused])
+def test_bad_sizes_rejected(lib, call):
+    assert call(lib, M=0) == w4.ERR_INVALID_VALUE
+    assert call(lib, N=0) == w4.ERR_INVALID_VALUE
+    assert call(lib, K=0) == w4.ERR_INVALID_VALUE
+    assert call(lib, M=-3) == w4.ERR_INVALID_VALUE
+    assert call(lib, M=17) == w4.ERR_UNSUPPORTED
+    assert call(lib, K=272) == w4.ERR_UNSUPPORTED      # multiple of 16 but not of 256
+    assert call(lib, K=128) == w4.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("call", [call_gemm, call_fused])
+def test_misaligned_pointers_rejected(lib, call):
+    assert call(lib, wq=P + 8) == w4.ERR_UNSUPPORTED
+    assert call(lib, ws=P + 4) == w4.ERR_UNSUPPORTED
+    assert call(lib, x=P + 2) == w4.ERR_UNSUPPORTED
+    assert call(lib, g=P + 2) == w4.ERR_UNSUPPORTED
+    assert call(lib, y=P + 2) == w4.ERR_UNSUPPORTED
+
+
+def test_workspace_sizes(lib):
+    # small x: no split, no workspace
+    assert w4.workspace_size(1, 5120, 5120) == 0
+    assert w4.workspace_size_gate_up(7, 17408, 5120) == 0
+    # 8 rows of a 17408-wide x do not fit in LDS: K is split in two
+    assert w4.workspace_size(7, 5120, 17408) == 2 * 7 * 5120 * 4
+    assert w4.workspace_size(8, 5120, 17408) == 2 * 8 * 5120 * 4
+    assert w4.workspace_size_gate_up(8, 512, 17408) == 2 * 2 * 8 * 512 * 4
+    assert w4.workspace_size(17, 64, 256) == 0            # unsupported shape: 0
+
+
+def test_short_workspace_rejected(lib):
+    need = w4.workspace_size(8, 5120, 17408)
+    assert call_gemm(lib, M=8, N=5120, K=17408, work=P, wbytes=need - 1) == w4.ERR_INVALID_VALUE
+    assert call_gemm(lib, M=8, N=5120, K=17408, work=0, wbytes=need) == w4.ERR_INVALID_VALUE
+    assert call_gemm(lib, M=8, N=5120, K=17408, work=P + 4, wbytes=need) == w4.ERR_UNSUPPORTED
+
+
+def test_dequant_argument_checks(lib):
+    assert lib.w4a16_dequant(0, P, P, P, 4, 256, None) == w4.ERR_INVALID_VALUE
+    assert lib.w4a16_dequant(P, P, P, P, 0, 256, None) == w4.ERR_INVALID_VALUE
+    assert lib.w4a16_dequant(P, P, P, P, 4, 272, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_dequant(P, P, P, P + 4, 4, 256, None) == w4.ERR_UNSUPPORTED
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    wq = torch.zeros((4, 128), dtype=torch.uint8)
+    ws = torch.zeros((4, 16), dtype=torch.uint8)
+    g = torch.ones(1)
+    x = torch.zeros((1, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        w4.gemm(wq, ws, g, x)
