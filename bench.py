@@ -27,6 +27,34 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic_square_m1.json")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: a stored traffic measurement is used only if it
+    was taken on exactly these kernels."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_scaled_fp4_w4a16_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """Calibrated HBM bytes per launch of the square GEMV from the committed
+    rocprofv3 PMC runs, or None when absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
 
 
 def weight_bytes(N, K):
@@ -72,6 +100,9 @@ def time_calls(fns, cycles, warmup_cycles, stream):
 
 
 def bench_square(args, dev, stream):
+    """Square GEMV: one step = one call per weight copy (64 calls), captured
+    once in a HIP graph and replayed; also times the same calls launched
+    eagerly from Python for reference."""
     import torch
     import block_scaled_fp4_w4a16_amd as w4
     import synth
@@ -84,30 +115,49 @@ def bench_square(args, dev, stream):
     wss = replicate(to_dev_u8(ws, dev), copies)
     gs = replicate(torch.tensor([g], dtype=torch.float32, device=dev), copies)
     y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
-    fns = [lambda i=i: w4.gemm(wqs[i], wss[i], gs[i], x, y=y, stream=stream) for i in range(copies)]
+    bpc = weight_bytes(N, K)
+
+    def step(strm):
+        for i in range(copies):
+            w4.gemm(wqs[i], wss[i], gs[i], x, y=y, stream=strm)
+
+    # eager reference (Python launches each call)
+    step(stream)
     torch.cuda.synchronize()
-    # warmup steps, then exactly `steps` steps timed
-    for _ in range(args.warmup):
-        for f in fns:
-            f()
+    t_eager = time_calls([lambda: step(stream)], 3, 1, stream) / copies
+
+    # capture one step, replay `warmup` untimed and exactly `steps` timed
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        step(cap)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap):
+        step(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            graph.replay()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        for f in fns:
-            f()
-    end.record(stream)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        end.record(stream)
     end.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end)
     calls = args.steps * copies
     per_call = ms * 1e-3 / calls
-    bpc = weight_bytes(N, K)
     return dict(N=N, K=K, copies=copies, calls=calls, ms=ms, wall=wall, per_call=per_call,
-                bytes_per_call=bpc, gbs=bpc / per_call / 1e9)
+                bytes_per_call=bpc, gbs=bpc / per_call / 1e9, eager_per_call=t_eager,
+                eager_gbs=bpc / t_eager / 1e9)
 
 
 def bench_extra(dev, stream, cycles=10):
@@ -177,6 +227,53 @@ def cpu_baseline(seconds_target=12.0):
                        f"with {threads} OpenMP threads; {dt*1e3:.1f} ms/call")
 
 
+def copy_calibration(dev, mib=256, reps=4):
+    """A plain device-to-device copy of known size, run under the same PMC
+    passes as the GEMV to calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n * 4, "reps": reps}), flush=True)
+
+
+def ingest_pmc(d):
+    """Calibrated HBM traffic of the square GEMV from four rocprofv3 --pmc runs
+    under `d`: pmc_bench_FETCH_SIZE, pmc_bench_WRITE_SIZE (this script's default
+    workload) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE (--mode copy, a
+    256 MiB device copy).  Each counter (KiB per dispatch) is scaled by
+    (known copy bytes) / (what the counter reads for the copy)."""
+    import csv
+    import glob
+    import statistics
+
+    def values(sub, pred):
+        f = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)[0]
+        return [float(r["Counter_Value"]) for r in csv.DictReader(open(f)) if pred(r["Kernel_Name"])]
+
+    copy_kib = 256 * 1024
+    out = {"kernel_source_hash": kernel_source_hash(), "unit": "bytes per launch"}
+    total = 0.0
+    for ctr, copy_pred in (("FETCH_SIZE", lambda n: "copyBuffer" in n),
+                           ("WRITE_SIZE", lambda n: "copyBuffer" in n)):
+        gemm = statistics.median(values(f"pmc_bench_{ctr}", lambda n: "k_gemm" in n))
+        cal = statistics.median(values(f"pmc_copy_{ctr}", copy_pred))
+        factor = copy_kib / cal
+        out[ctr] = {"gemm_kib_per_dispatch": gemm, "copy_kib_per_dispatch": cal, "factor": round(factor, 4),
+                    "calibrated_bytes": round(gemm * factor * 1024)}
+        total += gemm * factor * 1024
+    out["bytes_per_launch"] = round(total)
+    out["algorithmic_bytes_per_launch"] = weight_bytes(5120, 5120)
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,7 +281,18 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--extra", action="store_true", help="also time the gate/up and down configs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "copy", "ingest-pmc"], default="bench",
+                    help="copy: run only the PMC calibration copy kernel; ingest-pmc: turn rocprofv3 "
+                         "FETCH_SIZE/WRITE_SIZE outputs (--pmc-dir) into profiles/traffic_square_m1.json")
+    ap.add_argument("--pmc-dir", default=None)
     args = ap.parse_args()
+    if args.mode == "ingest-pmc":
+        ingest_pmc(args.pmc_dir)
+        return
+    if args.mode == "copy":
+        import torch
+        copy_calibration(torch.device("cuda:0"))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
@@ -196,7 +304,8 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     r = bench_square(args, dev, stream)
-    log(f"[bench] square: {r['per_call']*1e6:.3f} us/call, {r['gbs']:.1f} GB/s")
+    log(f"[bench] square (graph replay): {r['per_call']*1e6:.3f} us/call, {r['gbs']:.1f} GB/s; "
+        f"eager: {r['eager_per_call']*1e6:.3f} us/call, {r['eager_gbs']:.1f} GB/s")
     extra = bench_extra(dev, stream) if args.extra else None
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
@@ -213,11 +322,14 @@ def main():
         "dtype": "nvfp4(e2m1+e4m3) x bf16 -> fp32 accumulate",
         "data": "synthetic (seeded N(0,0.02) weights NVFP4-encoded, N(0,1) bf16 activations)",
         "config": {"workload": "square projection GEMV, K=5120 N=5120 M=1, 64 byte-identical "
-                               "weight copies (943.7 MB) cycled per call",
+                               "weight copies (943.7 MB) cycled per call; one step = the 64 calls "
+                               "captured in one HIP graph and replayed",
                    "K": r["K"], "N": r["N"], "M": 1, "copies": r["copies"], "calls_timed": r["calls"],
-                   "us_per_call": round(r["per_call"] * 1e6, 3)},
+                   "us_per_call": round(r["per_call"] * 1e6, 3),
+                   "eager_us_per_call": round(r["eager_per_call"] * 1e6, 3),
+                   "eager_gbs": round(r["eager_gbs"], 1)},
         "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": stored_traffic()},
         "cpu_baseline": cpu,
     }
     if extra is not None:

@@ -135,7 +135,11 @@ def gemm(wq, ws, g, x, y=None, workspace=None, stream=None):
     _check(y, "y", torch.bfloat16, 2)
     if tuple(y.shape) != (M, N):
         raise ValueError(f"y must be ({M}, {N})")
-    workspace, wbytes = _workspace(workspace, workspace_size(M, N, K) if M <= MAX_M else 0, x.device)
+    if workspace is None:
+        need = workspace_size(M, N, K) if M <= MAX_M else 0
+        workspace, wbytes = _workspace(None, need, x.device)
+    else:
+        workspace, wbytes = _workspace(workspace, 1, x.device)
     st = lib().w4a16_gemm(_ptr(wq), _ptr(ws), _ptr(g), _ptr(x), _ptr(y), M, N, K,
                           _ptr(workspace), wbytes, _stream(stream))
     if st != OK:

@@ -34,13 +34,66 @@ constexpr size_t kMaxLds = 160 * 1024;
 // How one matmul call is launched.
 struct Plan {
   bool mfma;   // false: VALU kernel (M <= 3); true: 4x4x4 MFMA kernel
-  int L;       // VALU: lanes per weight row (8, 16 or 32)
+  int lr;      // VALU: lanes per weight row L; MFMA: row quads per task R
+  int D;       // chunk loads in flight per lane (ring depth)
   int W;       // waves per workgroup
+  int LB;      // launch bound the kernel was compiled for (>= 64 * W)
   int nrb;     // row blocks
   int S;       // K-slices (split-K factor); grid = nrb * S workgroups
   size_t lds;  // dynamic LDS bytes per workgroup
   size_t ws;   // workspace bytes (fp32 partials) when S > 1
 };
+
+// ---- kernel registry ---------------------------------------------------------
+// Every compiled variant, keyed by its template parameters.  The planner only
+// picks variants that are listed here.
+struct KernEntry {
+  bool mfma;
+  int rows;   // VALU: MT (= M); MFMA: P (activation-row passes of 4)
+  int lr, D;
+  bool fused;
+  int LB;
+  const void* fn;
+};
+
+#define W4A16_VE(MT, L, D, F, LB) \
+  {false, MT, L, D, F, LB, reinterpret_cast<const void*>(&k_gemm_valu<MT, L, D, F, LB>)},
+#define W4A16_ME(P, R, D, F, LB) \
+  {true, P, R, D, F, LB, reinterpret_cast<const void*>(&k_gemm_mfma<P, R, D, F, LB>)},
+#define W4A16_VALU_ALL_MT(L, D, F, LB) W4A16_VE(1, L, D, F, LB) W4A16_VE(2, L, D, F, LB) W4A16_VE(3, L, D, F, LB)
+#define W4A16_MFMA_ALL_P(R, D, F, LB) \
+  W4A16_ME(1, R, D, F, LB) W4A16_ME(2, R, D, F, LB) W4A16_ME(3, R, D, F, LB) W4A16_ME(4, R, D, F, LB)
+
+#ifdef W4A16_TUNING
+#define W4A16_VALU_SET(F)                                                          \
+  W4A16_VALU_ALL_MT(8, 4, F, 1024) W4A16_VALU_ALL_MT(8, 8, F, 512)                 \
+  W4A16_VALU_ALL_MT(16, 4, F, 1024) W4A16_VALU_ALL_MT(16, 8, F, 512)               \
+  W4A16_VALU_ALL_MT(16, 8, F, 1024) W4A16_VALU_ALL_MT(16, 12, F, 512)              \
+  W4A16_VALU_ALL_MT(16, 16, F, 512)                                                \
+  W4A16_VALU_ALL_MT(32, 4, F, 1024) W4A16_VALU_ALL_MT(32, 8, F, 512)               \
+  W4A16_VALU_ALL_MT(32, 8, F, 1024) W4A16_VALU_ALL_MT(32, 12, F, 512)              \
+  W4A16_VALU_ALL_MT(32, 16, F, 512) W4A16_VALU_ALL_MT(32, 5, F, 1024)
+#define W4A16_MFMA_SET(F)                                                          \
+  W4A16_MFMA_ALL_P(1, 8, F, 512) W4A16_MFMA_ALL_P(1, 16, F, 512)                   \
+  W4A16_MFMA_ALL_P(2, 4, F, 512) W4A16_MFMA_ALL_P(2, 8, F, 512)                    \
+  W4A16_MFMA_ALL_P(2, 8, F, 1024) W4A16_MFMA_ALL_P(4, 4, F, 512)
+#else
+#define W4A16_VALU_SET(F)                                                          \
+  W4A16_VALU_ALL_MT(8, 4, F, 1024) W4A16_VALU_ALL_MT(16, 4, F, 1024)               \
+  W4A16_VALU_ALL_MT(32, 4, F, 1024)
+#define W4A16_MFMA_SET(F) W4A16_MFMA_ALL_P(2, 4, F, 512)
+#endif
+
+const KernEntry kKernels[] = {
+    W4A16_VALU_SET(false) W4A16_VALU_SET(true) W4A16_MFMA_SET(false) W4A16_MFMA_SET(true)};
+
+const KernEntry* find_kernel(bool mfma, int rows, int lr, int D, bool fused, int LB) {
+  for (const KernEntry& e : kKernels)
+    if (e.mfma == mfma && e.rows == rows && e.lr == lr && e.D == D && e.fused == fused &&
+        e.LB == LB)
+      return &e;
+  return nullptr;
+}
 
 // Waves per workgroup for `tasks` row groups: all of them when they fit,
 // otherwise the count in [4, wmax] that leaves the fewest idle wave slots.
@@ -58,90 +111,109 @@ int pick_waves(long long tasks, int wmax) {
   return best;
 }
 
+#ifdef W4A16_TUNING
+struct Override {
+  int enable, mfma, lr, D, W, LB, nrb, S;
+};
+Override g_override{};
+#endif
+
 // Kernel selection is a pure function of (M, N, K, fused) and the device's
 // compute-unit count.
 Plan plan_gemm(int M, int N, int K, bool fused) {
   Plan pl{};
   const int cus = cu_count();
   const int CR = K >> 5;  // 16-byte chunks per weight row (a multiple of 8)
-  int rows, RT;
-  if (M <= 3) {
-    pl.mfma = false;
-    int L = (CR % 16 == 0) ? 16 : 8;
-    if (CR % 32 == 0 && K >= 8192) L = 32;
-    pl.L = L;
+  int rows;
+  pl.mfma = M > 3;
+  // Launch rules from measured sweeps on MI355X over the benchmark shapes:
+  // shallow rings (4 chunk loads in flight per lane) with many waves beat deep
+  // rings; VALU kernels use up to 16 waves (128 VGPRs) and two workgroups per
+  // CU; MFMA kernels use 2 row quads per task and 8 waves per workgroup.
+  pl.D = 4;
+  int wmax;
+  if (!pl.mfma) {
+    pl.lr = (CR % 32 == 0) ? 32 : (CR % 16 == 0) ? 16 : 8;
+    pl.LB = 1024;
+    wmax = 16;
     rows = M;
-    RT = fused ? (64 / L) / 2 : 64 / L;
   } else {
-    pl.mfma = true;
-    pl.L = 16;
+    pl.lr = 2;
+    pl.LB = 512;
+    wmax = 8;
     rows = 4 * ((M + 3) / 4);
-    RT = fused ? 2 : 4;
   }
+#ifdef W4A16_TUNING
+  if (g_override.enable && (g_override.mfma != 0) == pl.mfma) {
+    pl.lr = g_override.lr;
+    pl.D = g_override.D;
+    pl.LB = g_override.LB;
+  }
+#endif
+  const int RT = pl.mfma ? (fused ? 2 : 4) * pl.lr : (fused ? (64 / pl.lr) / 2 : 64 / pl.lr);
+  // per-wave epilogue scratch (floats): VALU G*MT*NSEG, MFMA R*P*4*16
+  const size_t scr_per_wave =
+      pl.mfma ? (size_t)pl.lr * ((M + 3) / 4) * 4 * 16
+              : (size_t)(64 / pl.lr) * M * (pl.lr < 16 ? 1 : pl.lr / 16);
+  const size_t scr_max = scr_per_wave * sizeof(float) * (pl.LB / 64);
   // smallest K split whose x slice fits in LDS (and keeps whole chunks per lane)
   auto lds_bytes = [&](int S) { return (size_t)rows * (size_t)((CR / S) * 4 + 1) * 16; };
   int S = 1;
   for (; S < CR; ++S) {
     if (CR % S) continue;
-    if (!pl.mfma && (CR / S) % pl.L) continue;
-    if (lds_bytes(S) <= kMaxLds) break;
+    if (!pl.mfma && (CR / S) % pl.lr) continue;
+    if (lds_bytes(S) + scr_max <= kMaxLds) break;
   }
+#ifdef W4A16_TUNING
+  if (g_override.enable && (g_override.mfma != 0) == pl.mfma && g_override.S > 0) S = g_override.S;
+#endif
   pl.S = S;
-  pl.lds = lds_bytes(S);
   const long long groups = ((long long)N + RT - 1) / RT;  // row groups in total
-  long long nrb = cus / S > 0 ? cus / S : 1;
+  const int wg_per_cu = pl.mfma ? 1 : 2;
+  long long nrb = (long long)cus * wg_per_cu / S > 0 ? (long long)cus * wg_per_cu / S : 1;
+#ifdef W4A16_TUNING
+  if (g_override.enable && (g_override.mfma != 0) == pl.mfma && g_override.nrb > 0)
+    nrb = g_override.nrb;
+#endif
   if (nrb > groups) nrb = groups;
   pl.nrb = (int)nrb;
-  const long long tasks = (groups + nrb - 1) / nrb;        // row groups per block
-  pl.W = pick_waves(tasks, 8);
+  const long long tasks = (groups + nrb - 1) / nrb;  // row groups per block
+  // MFMA: always 8 waves (idle waves still share the x staging)
+  pl.W = pl.mfma ? wmax : pick_waves(tasks, wmax);
+#ifdef W4A16_TUNING
+  if (g_override.enable && (g_override.mfma != 0) == pl.mfma && g_override.W > 0)
+    pl.W = g_override.W;
+#endif
+  pl.lds = lds_bytes(S) + scr_per_wave * sizeof(float) * pl.W;
   pl.ws = S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1) : 0;
   return pl;
 }
 
-template <typename Kern>
-hipError_t launch(Kern kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-                  const MatArgs& args) {
+hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                  MatArgs args) {
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kernel, grid, block, lds, stream, args);
+  void* argv[] = {&args};
+  hipError_t e = hipLaunchKernel(fn, grid, block, argv, lds, stream);
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 
-template <bool FUSED>
-hipError_t dispatch(const Plan& pl, hipStream_t s, const MatArgs& a) {
-  constexpr int DV = 8;  // VALU ring depth (chunk loads in flight per lane)
-  constexpr int DM = 8;  // MFMA ring depth
-  const dim3 grid((unsigned)(pl.nrb * pl.S)), block((unsigned)(pl.W * 64));
-  hipError_t e;
-  if (!pl.mfma) {
-#define W4A16_VALU(MT)                                                                    \
-  switch (pl.L) {                                                                         \
-    case 8: e = launch(k_gemm_valu<MT, 8, DV, FUSED>, grid, block, pl.lds, s, a); break;   \
-    case 16: e = launch(k_gemm_valu<MT, 16, DV, FUSED>, grid, block, pl.lds, s, a); break; \
-    default: e = launch(k_gemm_valu<MT, 32, DV, FUSED>, grid, block, pl.lds, s, a); break; \
-  }
-    switch (a.M) {
-      case 1: W4A16_VALU(1) break;
-      case 2: W4A16_VALU(2) break;
-      default: W4A16_VALU(3) break;
-    }
-#undef W4A16_VALU
-  } else {
-    switch ((a.M + 3) / 4) {
-      case 1: e = launch(k_gemm_mfma<1, DM, FUSED>, grid, block, pl.lds, s, a); break;
-      case 2: e = launch(k_gemm_mfma<2, DM, FUSED>, grid, block, pl.lds, s, a); break;
-      case 3: e = launch(k_gemm_mfma<3, DM, FUSED>, grid, block, pl.lds, s, a); break;
-      default: e = launch(k_gemm_mfma<4, DM, FUSED>, grid, block, pl.lds, s, a); break;
-    }
-  }
+hipError_t dispatch(const Plan& pl, bool fused, hipStream_t s, const MatArgs& a) {
+  const int rows = pl.mfma ? (a.M + 3) / 4 : a.M;
+  const KernEntry* k = find_kernel(pl.mfma, rows, pl.lr, pl.D, fused, pl.LB);
+  if (!k || pl.W * 64 > pl.LB) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)pl.nrb, (unsigned)pl.S), block((unsigned)(pl.W * 64));
+  hipError_t e = launch(k->fn, grid, block, pl.lds, s, a);
   if (e != hipSuccess || pl.S == 1) return e;
   const long long MN = (long long)a.M * a.N;
   long long nb = (MN + 255) / 256;
   if (nb > 4LL * cu_count()) nb = 4LL * cu_count();
-  return launch(k_combine<FUSED>, dim3((unsigned)nb), dim3(256), 0, s, a);
+  const void* comb = fused ? reinterpret_cast<const void*>(&k_combine<true>)
+                           : reinterpret_cast<const void*>(&k_combine<false>);
+  return launch(comb, dim3((unsigned)nb), dim3(256), 0, s, a);
 }
 
 w4a16_status_t check_shape(int M, int N, int K) {
@@ -163,10 +235,12 @@ w4a16_status_t run_matmul(MatArgs a, bool fused, void* workspace, size_t workspa
   if (workspace_bytes < pl.ws || (pl.ws > 0 && workspace == nullptr))
     return W4A16_ERR_INVALID_VALUE;
   if (pl.ws > 0 && !aligned(workspace, 16)) return W4A16_ERR_UNSUPPORTED;
-  a.nrb = pl.nrb;
+  a.rq = a.N / pl.nrb;
+  a.rr = a.N % pl.nrb;
   a.S = pl.S;
+  a.CRS = (a.K >> 5) / pl.S;
   a.part = static_cast<float*>(workspace);
-  const hipError_t e = fused ? dispatch<true>(pl, stream, a) : dispatch<false>(pl, stream, a);
+  const hipError_t e = dispatch(pl, fused, stream, a);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
@@ -263,5 +337,25 @@ const char* w4a16_status_string(w4a16_status_t status) {
 }
 
 int w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+#ifdef W4A16_TUNING
+// Tuning builds only (not part of the ABI): force launch parameters for the
+// kernel family `mfma` (0 = VALU, 1 = MFMA); enable = 0 restores the planner.
+// Returns 1 if the requested variant is compiled in.
+__attribute__((visibility("default"))) int w4a16_tuning_set(int enable, int mfma, int lr, int D,
+                                                             int W, int LB, int nrb, int S) {
+  g_override = Override{enable, mfma, lr, D, W, LB, nrb, S};
+  if (!enable) return 1;
+  for (const KernEntry& e : kKernels)
+    if (e.mfma == (mfma != 0) && e.lr == lr && e.D == D && e.LB == LB) return 1;
+  return 0;
+}
+#endif
+#ifdef W4A16_TRACE
+// Trace builds only: device buffer for the per-wave timeline stamps (NULL = off).
+__attribute__((visibility("default"))) int w4a16_trace_set(void* buf) {
+  return hipMemcpyToSymbol(HIP_SYMBOL(w4a16_trace), &buf, sizeof(buf)) == hipSuccess ? 1 : 0;
+}
+#endif
 
 }  // extern "C"

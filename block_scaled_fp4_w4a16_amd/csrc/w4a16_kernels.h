@@ -40,13 +40,14 @@ struct MatArgs {
   const uint16_t* x;
   uint16_t* y;
   int M, N, K;
-  // Grid: nrb row blocks x S K-slices; workgroup b works on row block b / S
-  // (rows [rb*N/nrb, (rb+1)*N/nrb)) and K-slice b % S (chunks
-  // [s*CR/S, (s+1)*CR/S) of every row, CR = K/32).  With S > 1 the workgroup
-  // writes fp32 partial sums part[s][M][N] (fused: gate partials, then up
-  // partials at part + S*M*N) instead of y, and k_combine finishes them.
-  int nrb;
-  int S;
+  // Grid: (row blocks) x (S K-slices).  Row block rb = blockIdx.x owns
+  // rq + (rb < rr) rows starting at rb*rq + min(rb, rr); K-slice ks =
+  // blockIdx.y covers chunks [ks*CRS, (ks+1)*CRS) of every row (a chunk is
+  // 32 inputs).  With S > 1 the workgroup writes fp32 partial sums
+  // part[ks][M][N] (fused: gate partials, then up partials at part + S*M*N)
+  // instead of y, and k_combine finishes them.
+  int rq, rr;
+  int S, CRS;
   float* part;
 };
 
@@ -90,52 +91,114 @@ W4A16_DEV uint16_t f32_to_bf16(float f) {
 
 W4A16_DEV float silu(float v) { return v / (1.0f + expf(-v)); }
 
+// v + (v of another lane chosen by a DPP control; all lanes stay active)
+template <int CTRL>
+W4A16_DEV float dpp_add(float v) {
+  return v + __builtin_bit_cast(
+                 float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// DPP controls (gfx9): quad_perm [1,0,3,2], [2,3,0,1]; row_half_mirror; row_ror:n
+constexpr int kDppQuadXor1 = 0xB1, kDppQuadXor2 = 0x4E, kDppHalfMirror = 0x141;
+constexpr int kDppRor1 = 0x121, kDppRor2 = 0x122, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+// Sum over each aligned group of `N` consecutive lanes (N = 8 or 16); every
+// lane of the group receives the group total.
+template <int N>
+W4A16_DEV float group_allreduce(float v) {
+  if (N == 8) {
+    v = dpp_add<kDppQuadXor1>(v);
+    v = dpp_add<kDppQuadXor2>(v);
+    return dpp_add<kDppHalfMirror>(v);
+  }
+  v = dpp_add<kDppRor8>(v);
+  v = dpp_add<kDppRor4>(v);
+  v = dpp_add<kDppRor2>(v);
+  return dpp_add<kDppRor1>(v);
+}
+
+#ifdef W4A16_TRACE
+// Timeline probe for tuning builds: per wave, lane i < 6 stores stamp i
+// (s_memrealtime, 100 MHz) to w4a16_trace[(wave id) * 8 + i] with a vector store.
+__device__ unsigned long long* w4a16_trace;
+#define W4A16_STAMP(var) const unsigned long long var = wall_clock64()
+#define W4A16_TRACE_STORE(t0, t1, t2, t3, t4, t5)                                            \
+  if (w4a16_trace) {                                                                        \
+    const unsigned long long tv[6] = {t0, t1, t2, t3, t4, t5};                              \
+    const int ln = threadIdx.x & 63;                                                        \
+    unsigned long long mine = 0;                                                            \
+    for (int i = 0; i < 6; ++i) mine = ln == i ? tv[i] : mine;                              \
+    if (ln < 6) w4a16_trace[((size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 8 + ln] = mine; \
+  }
+#else
+#define W4A16_STAMP(var) const unsigned long long var = 0
+#define W4A16_TRACE_STORE(t0, t1, t2, t3, t4, t5)
+#endif
+
+// Orders this wave's LDS writes before its following LDS reads (a wave's LDS
+// operations execute in order; this only stops the compiler reordering).
+W4A16_DEV void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Position of 16-byte unit q (0..3) of x-chunk c inside an LDS x row for the
 // VALU kernel.  Lanes read consecutive chunks; the XOR spreads the four units
 // of neighbouring chunks over distinct bank groups (for 8- and 16-lane passes).
 W4A16_DEV int xsw(int c, int q) { return 4 * c + (q ^ (((c >> 1) ^ (c >> 2)) & 3)); }
 
-// Number of 16-byte x units each thread loads before the weight prologue is
-// issued (so that staging x in LDS never waits on the weight loads).
-constexpr int kXPre = 8;
-
 // Stage `rows` rows of x (K bf16 each; rows >= M are zero) into LDS units
-// xs[m*RSU + pos(cu)].  Phase 1 issues the first kXPre units per thread and
-// returns them in xr; phase 2 (after the caller has issued its weight loads)
-// writes them and handles any remainder.
+// xs[m*RSU + pos(cu)].  Phase 1 loads the first XMAX units per thread into
+// registers *before* the caller issues its weight prologue, so that storing
+// them (phase 2) waits only for x, since loads complete in order; units beyond
+// XMAX per thread (only for very wide x) are staged after the prologue.
 // The slice is `upr` units per row starting at unit u0 of each x row (a row
-// of x has K/8 units).
-W4A16_DEV void x_stage_issue(uint4 (&xr)[kXPre], const uint16_t* x, int M, int rows, int K,
+// of x has K/8 units); unit u of the staged block is (row u / upr, column
+// u % upr).  Thread tid handles units tid, tid + nthr, ...; the (row, column)
+// pair is advanced incrementally (no division per unit).
+struct XCursor {
+  int m, cu;
+  W4A16_DEV void init(int tid, int upr) {
+    m = tid / upr;
+    cu = tid - m * upr;
+  }
+  W4A16_DEV void advance(int nthr, int upr) {
+    cu += nthr;
+    while (cu >= upr) {
+      cu -= upr;
+      ++m;
+    }
+  }
+};
+template <int XMAX>
+W4A16_DEV void x_stage_issue(uint4 (&xr)[XMAX], const uint16_t* x, int M, int rows, int K,
                              int u0, int upr, int tid, int nthr) {
   const uint4* xg = reinterpret_cast<const uint4*>(x);
+  XCursor c;
+  c.init(tid, upr);
 #pragma unroll
-  for (int i = 0; i < kXPre; ++i) {
-    const int u = tid + i * nthr;
-    const int m = u / upr, cu = u - m * upr;
-    xr[i] = (u < rows * upr && m < M) ? xg[(size_t)m * (K >> 3) + u0 + cu]
-                                      : make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < XMAX; ++i) {
+    xr[i] = (c.m < rows && c.m < M) ? xg[(size_t)c.m * (K >> 3) + u0 + c.cu]
+                                    : make_uint4(0u, 0u, 0u, 0u);
+    c.advance(nthr, upr);
   }
 }
-template <typename Pos>
-W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[kXPre], const uint16_t* x, int M,
+template <int XMAX, typename Pos>
+W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[XMAX], const uint16_t* x, int M,
                              int rows, int K, int u0, int upr, int RSU, int tid, int nthr,
                              Pos pos) {
   const uint4* xg = reinterpret_cast<const uint4*>(x);
+  XCursor c;
+  c.init(tid, upr);
 #pragma unroll
-  for (int i = 0; i < kXPre; ++i) {
-    const int u = tid + i * nthr;
-    if (u < rows * upr) {
-      const int m = u / upr, cu = u - m * upr;
-      xs[m * RSU + pos(cu)] = xr[i];
-    }
+  for (int i = 0; i < XMAX; ++i) {
+    if (c.m < rows) xs[c.m * RSU + pos(c.cu)] = xr[i];
+    c.advance(nthr, upr);
   }
-  for (int u = tid + kXPre * nthr; u < rows * upr; u += nthr) {
-    const int m = u / upr, cu = u - m * upr;
-    xs[m * RSU + pos(cu)] =
-        m < M ? xg[(size_t)m * (K >> 3) + u0 + cu] : make_uint4(0u, 0u, 0u, 0u);
-  }
+  for (; c.m < rows; c.advance(nthr, upr))
+    xs[c.m * RSU + pos(c.cu)] =
+        c.m < M ? xg[(size_t)c.m * (K >> 3) + u0 + c.cu] : make_uint4(0u, 0u, 0u, 0u);
 }
-
 
 // ---------------------------------------------------------------------------
 // VALU kernel, M = MT in {1, 2, 3}.
@@ -153,21 +216,21 @@ W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[kXPre], const uint16_t
 // (swizzled) and are read with 128-bit LDS loads; lanes of different slots
 // read the same x (broadcast).
 // ---------------------------------------------------------------------------
-template <int MT, int L, int D, bool FUSED>
-__global__ void __launch_bounds__(512) k_gemm_valu(MatArgs a) {
+template <int MT, int L, int D, bool FUSED, int LB>
+__global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
+  W4A16_STAMP(t_start);
   extern __shared__ uint4 xs[];
   constexpr int G = 64 / L;
   constexpr int RT = FUSED ? G / 2 : G;
   const int W = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int K = a.K, CR = K >> 5, S = a.S;
-  const int ks = blockIdx.x % S;
-  const long long rb = blockIdx.x / S;
-  const int CRS = CR / S;                // chunks per row in this K-slice
+  const int K = a.K, S = a.S, CRS = a.CRS;  // CRS: chunks per row in this K-slice
+  const int ks = blockIdx.y, rb = blockIdx.x;
   const int c0 = ks * CRS;               // first chunk of the slice
   const int CPL = CRS / L, RSU = (CRS << 2) + 1;
-  const int row_lo = (int)(rb * a.N / a.nrb), row_hi = (int)((rb + 1) * a.N / a.nrb);
+  const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
+  const int row_hi = row_lo + a.rq + (rb < a.rr ? 1 : 0);
   const int ntasks = (row_hi - row_lo + RT - 1) / RT;
   const int p = lane % L, r = lane / L;
   const int srow = FUSED ? (r % (G / 2)) : r;
@@ -176,8 +239,6 @@ __global__ void __launch_bounds__(512) k_gemm_valu(MatArgs a) {
   const uint8_t* ws = is_up ? a.ws1 : a.ws0;
   const int my_tasks = wv < ntasks ? (ntasks - 1 - wv) / W + 1 : 0;
   const int T = my_tasks * CPL;  // chunk steps of this wave (uniform)
-  const float g0 = *a.g0;
-  const float g1 = FUSED ? *a.g1 : 1.0f;
 
   // ---- issue cursor: (task it_i, step jj_i) -> row pointers -------------
   const uint4* qp;
@@ -208,48 +269,67 @@ __global__ void __launch_bounds__(512) k_gemm_valu(MatArgs a) {
   };
   // x -> LDS (rows of K bf16; 16-byte units, swizzled): x loads first, then
   // the weight prologue, then the LDS stores
-  uint4 xr[kXPre];
+  constexpr int XMAX = LB > 512 ? 8 : 16;
+  uint4 xr[XMAX];
   auto xpos = [](int cu) { return xsw(cu >> 2, cu & 3); };
   x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, tid, blockDim.x);
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
+  W4A16_STAMP(t_issued);
   x_stage_store(xs, xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, RSU, tid, blockDim.x, xpos);
   __syncthreads();
+  W4A16_STAMP(t_barrier);
+#ifdef W4A16_TRACE
+  unsigned long long t_first = 0;
+#endif
 
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
   int it_c = 0, jj_c = 0;
 
+  // Task epilogue: sum each row slot's L lanes (DPP inside groups of up to 16
+  // lanes, then the NSEG group totals through a small per-wave LDS scratch),
+  // then one lane per output finishes it.
+  constexpr int GL = L < 16 ? L : 16;     // lanes summed by DPP
+  constexpr int NSEG = L / GL;            // groups per row slot
+  float* scr = reinterpret_cast<float*>(xs + MT * RSU) + wv * (G * MT * NSEG);
   auto finish_task = [&]() {
+    const int seg = p / GL;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-#pragma unroll
-      for (int off = L / 2; off >= 1; off >>= 1) acc[m] += __shfl_xor(acc[m], off, 64);
+      const float v = group_allreduce<GL>(acc[m]);
+      if ((p % GL) == 0) scr[(r * MT + m) * NSEG + seg] = v;
+      acc[m] = 0.0f;
     }
-    const int row = row_lo + (wv + W * it_c) * RT + srow;
-    if (S > 1) {
-      // partial sums of this K-slice; gate and up land in separate planes
-      float* dst = a.part + ((size_t)(is_up ? S : 0) + ks) * (size_t)a.M * a.N;
-      if (p == 0 && row < row_hi) {
+    wave_lds_sync();
+    const int base = row_lo + (wv + W * it_c) * RT;
+    // 1/g is read here, at the first use, so that no global load is waited
+    // for before the weight stream starts
+    const float ig0 = 1.0f / *a.g0;
+    const float ig1 = FUSED ? 1.0f / *a.g1 : 1.0f;
+    for (int o = lane; o < RT * MT; o += 64) {
+      const int rr = o / MT, m = o - rr * MT;   // output row (within task), activation row
+      float v = 0.0f, u = 0.0f;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) dst[(size_t)m * a.N + row] = acc[m];
+      for (int sg = 0; sg < NSEG; ++sg) v += scr[(rr * MT + m) * NSEG + sg];
+      if (FUSED) {
+#pragma unroll
+        for (int sg = 0; sg < NSEG; ++sg) u += scr[((rr + G / 2) * MT + m) * NSEG + sg];
       }
-    } else if (FUSED) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const float upv = __shfl(acc[m], (lane + (G / 2) * L) & 63, 64);
-        if (!is_up && p == 0 && row < row_hi)
-          a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(acc[m] / g0) * (upv / g1));
-      }
-    } else {
-      if (p == 0 && row < row_hi) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) a.y[(size_t)m * a.N + row] = f32_to_bf16(acc[m] / g0);
+      const int row = base + rr;
+      if (row < row_hi) {
+        if (S > 1) {
+          a.part[((size_t)ks * a.M + m) * a.N + row] = v;
+          if (FUSED) a.part[((size_t)(S + ks) * a.M + m) * a.N + row] = u;
+        } else if (FUSED) {
+          a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v * ig0) * (u * ig1));
+        } else {
+          a.y[(size_t)m * a.N + row] = f32_to_bf16(v * ig0);
+        }
       }
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+    wave_lds_sync();
   };
 
   for (int s0 = 0; s0 < T; s0 += D) {
@@ -262,10 +342,19 @@ __global__ void __launch_bounds__(512) k_gemm_valu(MatArgs a) {
         const uint32_t sc = sb[d];
         const int c = p + L * jj_c;
         uint4 xv[MT][4];
+        if (L >= 16) {
+          // c and p agree in bits 0..3, so the swizzle term is fixed per lane
+          const int hp = ((p >> 1) ^ (p >> 2)) & 3;
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+          for (int m = 0; m < MT; ++m)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) xv[m][u] = xs[m * RSU + xsw(c, u)];
+            for (int u = 0; u < 4; ++u) xv[m][u] = xs[m * RSU + 4 * c + (u ^ hp)];
+        } else {
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) xv[m][u] = xs[m * RSU + xsw(c, u)];
+        }
         const float s_lo = e4m3_to_f32<0>(sc), s_hi = e4m3_to_f32<1>(sc);
         float blo[MT], bhi[MT];
 #pragma unroll
@@ -294,6 +383,9 @@ __global__ void __launch_bounds__(512) k_gemm_valu(MatArgs a) {
           acc[m] = fmaf(blo[m], s_lo, acc[m]);
           acc[m] = fmaf(bhi[m], s_hi, acc[m]);
         }
+#ifdef W4A16_TRACE
+        if (t_first == 0) t_first = wall_clock64();
+#endif
         if (++jj_c == CPL) {
           finish_task();
           jj_c = 0;
@@ -303,6 +395,10 @@ __global__ void __launch_bounds__(512) k_gemm_valu(MatArgs a) {
       issue(d);
     }
   }
+  W4A16_STAMP(t_end);
+#ifdef W4A16_TRACE
+  W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, (unsigned long long)T);
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -316,54 +412,60 @@ __global__ void __launch_bounds__(512) k_gemm_valu(MatArgs a) {
 // scale block, so the E4M3 scale multiplies the fp32 MFMA result of its block
 // (4 MFMAs per block, one FMA per result element).
 //
-// Lane (beta, j) reads chunks beta, beta+16, ... of weight row j of the task
-// (16 lanes x 16 B = 256 contiguous bytes per row per load) and the x slice of
-// activation row 4*pp + j for the same chunk from LDS.  Tasks are 4 weight
-// rows (fused: 2 gate rows and the same 2 up rows).
+// A task is R quads of weight rows (fused: R pairs of gate rows and the same
+// pairs of up rows).  Lane (beta, j) reads chunk beta, beta+16, ... of row j of
+// every quad (16 lanes x 16 B = 256 contiguous bytes per row per load) and,
+// once per chunk, the x slice of activation row 4*pp + j from LDS, which then
+// feeds the MFMAs of all R quads.
 // ---------------------------------------------------------------------------
-template <int P, int D, bool FUSED>
-__global__ void __launch_bounds__(512) k_gemm_mfma(MatArgs a) {
+template <int P, int R, int D, bool FUSED, int LB>
+__global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
+  W4A16_STAMP(t_start);
   extern __shared__ uint4 xs[];
-  constexpr int RT = FUSED ? 2 : 4;
+  constexpr int QS = FUSED ? 2 : 4;      // output rows per quad
+  constexpr int RT = QS * R;             // output rows per task
   const int W = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int K = a.K, CR = K >> 5, S = a.S;
-  const int ks = blockIdx.x % S;
-  const long long rb = blockIdx.x / S;
-  const int CRS = CR / S;                // chunks per row in this K-slice
+  const int K = a.K, S = a.S, CRS = a.CRS;  // CRS: chunks per row in this K-slice
+  const int ks = blockIdx.y, rb = blockIdx.x;
   const int c0 = ks * CRS;
   const int CPL = (CRS + 15) >> 4, RSU = (CRS << 2) + 1;
-  const int row_lo = (int)(rb * a.N / a.nrb), row_hi = (int)((rb + 1) * a.N / a.nrb);
+  const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
+  const int row_hi = row_lo + a.rq + (rb < a.rr ? 1 : 0);
   const int ntasks = (row_hi - row_lo + RT - 1) / RT;
   const int beta = lane >> 2, j = lane & 3;
-  const int srow = FUSED ? (j & 1) : j;
+  const int jr = FUSED ? (j & 1) : j;    // row within the quad
   const bool is_up = FUSED && (j >= 2);
   const uint8_t* wq = is_up ? a.wq1 : a.wq0;
   const uint8_t* ws = is_up ? a.ws1 : a.ws0;
   const int my_tasks = wv < ntasks ? (ntasks - 1 - wv) / W + 1 : 0;
   const int T = my_tasks * CPL;
   const bool ragged = (CRS & 15) != 0;
-  const float g0 = *a.g0;
-  const float g1 = FUSED ? *a.g1 : 1.0f;
 
-  const uint4* qp;
-  const uint16_t* sp;
+  const uint4* qp[R];
+  const uint16_t* sp[R];
   int s_i = 0, it_i = 0, jj_i = 0;
   auto set_task = [&](int it) {
-    int row = row_lo + (wv + W * it) * RT + srow;
-    row = row < row_hi ? row : row_hi - 1;
-    qp = reinterpret_cast<const uint4*>(wq + (size_t)row * (size_t)(K >> 1)) + c0;
-    sp = reinterpret_cast<const uint16_t*>(ws + (size_t)row * (size_t)(K >> 4)) + c0;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      int row = row_lo + (wv + W * it) * RT + rr * QS + jr;
+      row = row < row_hi ? row : row_hi - 1;
+      qp[rr] = reinterpret_cast<const uint4*>(wq + (size_t)row * (size_t)(K >> 1)) + c0;
+      sp[rr] = reinterpret_cast<const uint16_t*>(ws + (size_t)row * (size_t)(K >> 4)) + c0;
+    }
   };
   set_task(0);
-  uint4 qb[D];
-  uint32_t sb[D];
+  uint4 qb[D][R];
+  uint32_t sb[D][R];
   auto issue = [&](int d) {
     int c = beta + 16 * jj_i;
     c = c < CRS ? c : CRS - 1;
-    qb[d] = qp[c];
-    sb[d] = sp[c];
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      qb[d][rr] = qp[rr][c];
+      sb[d][rr] = sp[rr][c];
+    }
     if (s_i + 1 < T) {
       ++s_i;
       if (++jj_i == CPL) {
@@ -373,102 +475,133 @@ __global__ void __launch_bounds__(512) k_gemm_mfma(MatArgs a) {
       }
     }
   };
-  // x -> LDS: rows 0..4P-1 (rows >= M are zero), K bf16 + 16 B pad per row
-  uint4 xr[kXPre];
+  // x -> LDS: rows 0..4P-1 (rows >= M are zero), 16 B pad per row
+  constexpr int XMAX = LB > 512 ? 8 : 16;
+  uint4 xr[XMAX];
   auto xpos = [](int cu) { return cu; };
   x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, tid, blockDim.x);
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
+  W4A16_STAMP(t_issued);
   x_stage_store(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, RSU, tid, blockDim.x, xpos);
   __syncthreads();
+  W4A16_STAMP(t_barrier);
+#ifdef W4A16_TRACE
+  unsigned long long t_first = 0;
+#endif
 
-  float acc[P][4];
+  float acc[R][P][4];
 #pragma unroll
-  for (int pp = 0; pp < P; ++pp)
+  for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[pp][r] = 0.0f;
+    for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[rr][pp][r] = 0.0f;
   int it_c = 0, jj_c = 0;
 
+  // Task epilogue: for each of the V = R*P*4 accumulators, sum the 4 chunk
+  // columns inside each 16-lane row with DPP, park the 4 row totals per
+  // (value, weight row j) in a per-wave LDS scratch, then one lane per output
+  // adds them and finishes the output.
+  constexpr int V = R * P * 4;
+  float* scr = reinterpret_cast<float*>(xs + 4 * P * RSU) + wv * (V * 16);
   auto finish_task = [&]() {
+    const int row16 = lane >> 4;
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp)
+    for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v = acc[pp][r];
-        v += __shfl_xor(v, 4, 64);
-        v += __shfl_xor(v, 8, 64);
-        v += __shfl_xor(v, 16, 64);
-        v += __shfl_xor(v, 32, 64);
-        acc[pp][r] = v;
-      }
-    const int row = row_lo + (wv + W * it_c) * RT + srow;
+      for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * pp + r;
-        if (S > 1) {
-          float* dst = a.part + ((size_t)(is_up ? S : 0) + ks) * (size_t)a.M * a.N;
-          if (lane < 4 && row < row_hi && m < a.M) dst[(size_t)m * a.N + row] = acc[pp][r];
-        } else if (FUSED) {
-          const float upv = __shfl(acc[pp][r], (lane + 2) & 63, 64);
-          if (lane < 2 && row < row_hi && m < a.M)
-            a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(acc[pp][r] / g0) * (upv / g1));
-        } else {
-          if (lane < 4 && row < row_hi && m < a.M)
-            a.y[(size_t)m * a.N + row] = f32_to_bf16(acc[pp][r] / g0);
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[rr][pp][r];
+          v = dpp_add<kDppRor4>(v);
+          v = dpp_add<kDppRor8>(v);
+          const int vi = (rr * P + pp) * 4 + r;
+          if ((lane & 12) == 0) scr[(vi * 4 + j) * 4 + row16] = v;
+          acc[rr][pp][r] = 0.0f;
         }
-        acc[pp][r] = 0.0f;
+    wave_lds_sync();
+    const int base = row_lo + (wv + W * it_c) * RT;
+    const float ig0 = 1.0f / *a.g0;       // read at the first use (see the VALU kernel)
+    const float ig1 = FUSED ? 1.0f / *a.g1 : 1.0f;
+    constexpr int NJ = FUSED ? 2 : 4;      // output rows per quad
+    for (int o = lane; o < V * NJ; o += 64) {
+      const int vi = o / NJ, jo = o - vi * NJ;
+      const int rr = vi / (P * 4), m = vi % (P * 4);
+      const float4 pv = *reinterpret_cast<const float4*>(&scr[(vi * 4 + jo) * 4]);
+      const float v = (pv.x + pv.y) + (pv.z + pv.w);
+      float u = 0.0f;
+      if (FUSED) {
+        const float4 pu = *reinterpret_cast<const float4*>(&scr[(vi * 4 + jo + 2) * 4]);
+        u = (pu.x + pu.y) + (pu.z + pu.w);
       }
+      const int row = base + rr * QS + jo;
+      if (row < row_hi && m < a.M) {
+        if (S > 1) {
+          a.part[((size_t)ks * a.M + m) * a.N + row] = v;
+          if (FUSED) a.part[((size_t)(S + ks) * a.M + m) * a.N + row] = u;
+        } else if (FUSED) {
+          a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v * ig0) * (u * ig1));
+        } else {
+          a.y[(size_t)m * a.N + row] = f32_to_bf16(v * ig0);
+        }
+      }
+    }
+    wave_lds_sync();
   };
 
   for (int s0 = 0; s0 < T; s0 += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (s0 + d < T) {
-        uint4 q = qb[d];
-        const uint32_t sc = sb[d];
         int c = beta + 16 * jj_c;
-        if (ragged && c >= CRS) {
-          q = make_uint4(0u, 0u, 0u, 0u);
-          c = CRS - 1;
-        }
+        const bool dead = ragged && c >= CRS;  // lane past the end of a ragged slice
+        c = dead ? CRS - 1 : c;
         uint4 xv[P][4];
 #pragma unroll
         for (int pp = 0; pp < P; ++pp)
 #pragma unroll
           for (int u = 0; u < 4; ++u) xv[pp][u] = xs[(4 * pp + j) * RSU + 4 * c + u];
-        const float s_lo = e4m3_to_f32<0>(sc), s_hi = e4m3_to_f32<1>(sc);
-        f32x4_t C[P];
-        // word wi holds inputs 8wi..8wi+7 of the chunk: two MFMAs of 4 inputs
-#define W4A16_MFMA_WORD(word, wi)                                              \
-  {                                                                            \
-    const i16x4_t b0 = pack4(fp4x2_to_bf16x2<0>(word), fp4x2_to_bf16x2<1>(word)); \
-    const i16x4_t b1 = pack4(fp4x2_to_bf16x2<2>(word), fp4x2_to_bf16x2<3>(word)); \
-    _Pragma("unroll") for (int pp = 0; pp < P; ++pp) {                          \
-      C[pp] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(                            \
-          pack4(xv[pp][wi].x, xv[pp][wi].y), b0, C[pp], 0, 0, 0);                \
-      C[pp] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(                            \
-          pack4(xv[pp][wi].z, xv[pp][wi].w), b1, C[pp], 0, 0, 0);                \
-    }                                                                          \
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          uint4 q = qb[d][rr];
+          if (dead) q = make_uint4(0u, 0u, 0u, 0u);
+          const uint32_t sc = sb[d][rr];
+          const float s_lo = e4m3_to_f32<0>(sc), s_hi = e4m3_to_f32<1>(sc);
+          f32x4_t C[P];
+          // word wi holds inputs 8wi..8wi+7 of the chunk: two MFMAs of 4 inputs
+#define W4A16_MFMA_WORD(word, wi)                                                   \
+  {                                                                                 \
+    const i16x4_t b0 = pack4(fp4x2_to_bf16x2<0>(word), fp4x2_to_bf16x2<1>(word));   \
+    const i16x4_t b1 = pack4(fp4x2_to_bf16x2<2>(word), fp4x2_to_bf16x2<3>(word));   \
+    _Pragma("unroll") for (int pp = 0; pp < P; ++pp) {                              \
+      C[pp] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pack4(xv[pp][wi].x, xv[pp][wi].y), \
+                                                      b0, C[pp], 0, 0, 0);          \
+      C[pp] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pack4(xv[pp][wi].z, xv[pp][wi].w), \
+                                                      b1, C[pp], 0, 0, 0);          \
+    }                                                                               \
   }
 #pragma unroll
-        for (int pp = 0; pp < P; ++pp) C[pp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        W4A16_MFMA_WORD(q.x, 0)
-        W4A16_MFMA_WORD(q.y, 1)
+          for (int pp = 0; pp < P; ++pp) C[pp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          W4A16_MFMA_WORD(q.x, 0)
+          W4A16_MFMA_WORD(q.y, 1)
 #pragma unroll
-        for (int pp = 0; pp < P; ++pp)
+          for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[pp][r] = fmaf(C[pp][r], s_lo, acc[pp][r]);
+            for (int r = 0; r < 4; ++r) acc[rr][pp][r] = fmaf(C[pp][r], s_lo, acc[rr][pp][r]);
 #pragma unroll
-        for (int pp = 0; pp < P; ++pp) C[pp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        W4A16_MFMA_WORD(q.z, 2)
-        W4A16_MFMA_WORD(q.w, 3)
+          for (int pp = 0; pp < P; ++pp) C[pp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+          W4A16_MFMA_WORD(q.z, 2)
+          W4A16_MFMA_WORD(q.w, 3)
 #pragma unroll
-        for (int pp = 0; pp < P; ++pp)
+          for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[pp][r] = fmaf(C[pp][r], s_hi, acc[pp][r]);
+            for (int r = 0; r < 4; ++r) acc[rr][pp][r] = fmaf(C[pp][r], s_hi, acc[rr][pp][r]);
 #undef W4A16_MFMA_WORD
+        }
+#ifdef W4A16_TRACE
+        if (t_first == 0) t_first = wall_clock64();
+#endif
         if (++jj_c == CPL) {
           finish_task();
           jj_c = 0;
@@ -478,6 +611,10 @@ __global__ void __launch_bounds__(512) k_gemm_mfma(MatArgs a) {
       issue(d);
     }
   }
+  W4A16_STAMP(t_end);
+#ifdef W4A16_TRACE
+  W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, (unsigned long long)T);
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -488,8 +625,8 @@ __global__ void __launch_bounds__(512) k_gemm_mfma(MatArgs a) {
 template <bool FUSED>
 __global__ void __launch_bounds__(256) k_combine(MatArgs a) {
   const long long MN = (long long)a.M * a.N;
-  const float g0 = *a.g0;
-  const float g1 = FUSED ? *a.g1 : 1.0f;
+  const float ig0 = 1.0f / *a.g0;
+  const float ig1 = FUSED ? 1.0f / *a.g1 : 1.0f;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < MN;
        i += (long long)gridDim.x * blockDim.x) {
     float v = 0.0f;
@@ -497,9 +634,9 @@ __global__ void __launch_bounds__(256) k_combine(MatArgs a) {
     if (FUSED) {
       float u = 0.0f;
       for (int s = 0; s < a.S; ++s) u += a.part[(size_t)(a.S + s) * MN + i];
-      a.y[i] = f32_to_bf16(silu(v / g0) * (u / g1));
+      a.y[i] = f32_to_bf16(silu(v * ig0) * (u * ig1));
     } else {
-      a.y[i] = f32_to_bf16(v / g0);
+      a.y[i] = f32_to_bf16(v * ig0);
     }
   }
 }
