@@ -40,6 +40,8 @@ struct Plan {
   int LB;      // launch bound the kernel was compiled for (>= 64 * W)
   int nrb;     // row blocks
   int S;       // K-slices (split-K factor); grid = nrb * S workgroups
+  int rq, rr;  // rows per row block: rq, plus one for the first rr blocks
+  int kmax;    // segment slots per wave
   size_t lds;  // dynamic LDS bytes per workgroup
   size_t ws;   // workspace bytes (fp32 partials) when S > 1
 };
@@ -95,20 +97,23 @@ const KernEntry* find_kernel(bool mfma, int rows, int lr, int D, bool fused, int
   return nullptr;
 }
 
-// Waves per workgroup for `tasks` row groups: all of them when they fit,
-// otherwise the count in [4, wmax] that leaves the fewest idle wave slots.
-int pick_waves(long long tasks, int wmax) {
-  if (tasks <= wmax) return (int)(tasks > 0 ? tasks : 1);
-  int best = wmax;
-  long long best_waste = -1;
-  for (int w = wmax; w >= 4; --w) {
-    const long long waste = (tasks + w - 1) / w * w - tasks;
-    if (best_waste < 0 || waste < best_waste) {
-      best = w;
-      best_waste = waste;
-    }
+// Waves of kernel `fn` that fit on one CU at once as limited by its VGPR use
+// (512 VGPRs per SIMD lane, allocated in granules of 8; at most 8 waves per
+// SIMD).  Cached per registry entry; 32 if the attributes are unavailable.
+int g_waves_per_cu[sizeof(kKernels) / sizeof(kKernels[0])];
+int waves_per_cu(const KernEntry* k) {
+  const size_t i = (size_t)(k - kKernels);
+  int n = __atomic_load_n(&g_waves_per_cu[i], __ATOMIC_RELAXED);
+  if (n > 0) return n;
+  hipFuncAttributes attr{};
+  n = 32;
+  if (hipFuncGetAttributes(&attr, k->fn) == hipSuccess && attr.numRegs > 0) {
+    const int alloc = (attr.numRegs + 7) / 8 * 8;
+    const int per_simd = 512 / alloc < 8 ? 512 / alloc : 8;
+    n = 4 * (per_simd > 0 ? per_simd : 1);
   }
-  return best;
+  __atomic_store_n(&g_waves_per_cu[i], n, __ATOMIC_RELAXED);
+  return n;
 }
 
 #ifdef W4A16_TUNING
@@ -124,69 +129,105 @@ Plan plan_gemm(int M, int N, int K, bool fused) {
   Plan pl{};
   const int cus = cu_count();
   const int CR = K >> 5;  // 16-byte chunks per weight row (a multiple of 8)
-  int rows;
   pl.mfma = M > 3;
   // Launch rules from measured sweeps on MI355X over the benchmark shapes:
-  // shallow rings (4 chunk loads in flight per lane) with many waves beat deep
-  // rings; VALU kernels use up to 16 waves (128 VGPRs) and two workgroups per
-  // CU; MFMA kernels use 2 row quads per task and 8 waves per workgroup.
+  // shallow rings (4 chunk loads in flight per lane); one workgroup of 8
+  // waves per CU (x is staged into LDS once per workgroup, so fewer row
+  // blocks means less x traffic); VALU rows read by 16 lanes; MFMA tasks of
+  // 2 row quads.
   pl.D = 4;
-  int wmax;
+  int wmax, wg_per_cu;
   if (!pl.mfma) {
-    pl.lr = (CR % 32 == 0) ? 32 : (CR % 16 == 0) ? 16 : 8;
+    pl.lr = (CR % 16 == 0) ? 16 : 8;
     pl.LB = 1024;
-    wmax = 16;
-    rows = M;
+    wmax = 8;
+    wg_per_cu = 1;
   } else {
     pl.lr = 2;
     pl.LB = 512;
     wmax = 8;
-    rows = 4 * ((M + 3) / 4);
+    wg_per_cu = 1;
   }
+  bool force_w = false;
 #ifdef W4A16_TUNING
-  if (g_override.enable && (g_override.mfma != 0) == pl.mfma) {
+  const bool ov = g_override.enable && (g_override.mfma != 0) == pl.mfma;
+  if (ov) {
     pl.lr = g_override.lr;
     pl.D = g_override.D;
     pl.LB = g_override.LB;
+    if (g_override.W > 0) {
+      wmax = g_override.W;
+      force_w = true;
+    }
   }
 #endif
+  if (wmax > pl.LB / 64) wmax = pl.LB / 64;
+  // keep wg_per_cu workgroups resident together
+  const KernEntry* ke =
+      find_kernel(pl.mfma, pl.mfma ? (M + 3) / 4 : M, pl.lr, pl.D, fused, pl.LB);
+  if (!ke) return Plan{};
+  const int wocc = waves_per_cu(ke) / wg_per_cu;
+  int wcap = wmax < wocc ? wmax : wocc;
+  if (wcap < 1) wcap = 1;
+  const int xrows = pl.mfma ? 4 * ((M + 3) / 4) : M;        // staged x rows
   const int RT = pl.mfma ? (fused ? 2 : 4) * pl.lr : (fused ? (64 / pl.lr) / 2 : 64 / pl.lr);
-  // per-wave epilogue scratch (floats): VALU G*MT*NSEG, MFMA R*P*4*16
+  // per-wave floats: epilogue scratch (VALU G*MT*NSEG, MFMA R*P*4*16) and one
+  // segment partial (VALU G*MT, MFMA R*P*4*4)
   const size_t scr_per_wave =
       pl.mfma ? (size_t)pl.lr * ((M + 3) / 4) * 4 * 16
               : (size_t)(64 / pl.lr) * M * (pl.lr < 16 ? 1 : pl.lr / 16);
-  const size_t scr_max = scr_per_wave * sizeof(float) * (pl.LB / 64);
-  // smallest K split whose x slice fits in LDS (and keeps whole chunks per lane)
-  auto lds_bytes = [&](int S) { return (size_t)rows * (size_t)((CR / S) * 4 + 1) * 16; };
-  int S = 1;
-  for (; S < CR; ++S) {
-    if (CR % S) continue;
-    if (!pl.mfma && (CR / S) % pl.lr) continue;
-    if (lds_bytes(S) + scr_max <= kMaxLds) break;
-  }
-#ifdef W4A16_TUNING
-  if (g_override.enable && (g_override.mfma != 0) == pl.mfma && g_override.S > 0) S = g_override.S;
-#endif
-  pl.S = S;
+  const size_t seg_vals = pl.mfma ? (size_t)pl.lr * ((M + 3) / 4) * 16 : (size_t)(64 / pl.lr) * M;
   const long long groups = ((long long)N + RT - 1) / RT;  // row groups in total
-  const int wg_per_cu = pl.mfma ? 1 : 2;
-  long long nrb = (long long)cus * wg_per_cu / S > 0 ? (long long)cus * wg_per_cu / S : 1;
+  // smallest K split whose x slice, scratch and segment partials fit in LDS
+  // (VALU: whole chunk steps per lane)
+  for (int S = 1; S <= CR; ++S) {
+    if (CR % S) continue;
+    const int CRS = CR / S;
+    if (!pl.mfma && CRS % pl.lr) continue;
+    long long nrb = (long long)cus * wg_per_cu / S > 0 ? (long long)cus * wg_per_cu / S : 1;
 #ifdef W4A16_TUNING
-  if (g_override.enable && (g_override.mfma != 0) == pl.mfma && g_override.nrb > 0)
-    nrb = g_override.nrb;
+    if (ov && g_override.S > 0) {
+      if (S != g_override.S) continue;
+    }
+    if (ov && g_override.nrb > 0) nrb = g_override.nrb;
 #endif
-  if (nrb > groups) nrb = groups;
-  pl.nrb = (int)nrb;
-  const long long tasks = (groups + nrb - 1) / nrb;  // row groups per block
-  // MFMA: always 8 waves (idle waves still share the x staging)
-  pl.W = pl.mfma ? wmax : pick_waves(tasks, wmax);
-#ifdef W4A16_TUNING
-  if (g_override.enable && (g_override.mfma != 0) == pl.mfma && g_override.W > 0)
-    pl.W = g_override.W;
-#endif
-  pl.lds = lds_bytes(S) + scr_per_wave * sizeof(float) * pl.W;
-  pl.ws = S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1) : 0;
-  return pl;
+    if (nrb > groups) nrb = groups;
+    if (nrb > N) nrb = N;
+    const int rq = N / (int)nrb, rr = N % (int)nrb;
+    const long long ntasks = ((long long)rq + (rr > 0) + RT - 1) / RT;  // tasks of the largest block
+    const int CPL = pl.mfma ? (CRS + 15) / 16 : CRS / pl.lr;
+    const long long TS = ntasks * CPL;
+    // LDS bytes for W waves: x slice, per-wave scratch, segment slots and
+    // the task bookkeeping (two ints per segment slot, one per wave)
+    auto lds_for = [&](int W, long long* kmax_out) {
+      const long long steps = (TS + W - 1) / W;  // most steps of one wave
+      long long kmax = (steps - 1 + CPL - 1) / CPL + 1;
+      if (kmax > ntasks) kmax = ntasks;
+      if (kmax_out) *kmax_out = kmax;
+      return (size_t)xrows * (size_t)(CRS * 4 + 1) * 16 +
+             (scr_per_wave + (size_t)kmax * seg_vals) * sizeof(float) * W +
+             (2 * (size_t)kmax + 1) * sizeof(int) * W;
+    };
+    // the split is chosen for the largest wave count (so that it does not
+    // depend on the occupancy query), the wave count then by occupancy
+    const int Wfit = force_w ? wmax : (int)(TS < wmax ? TS : wmax);
+    if (lds_for(Wfit, nullptr) > kMaxLds && S < CR) continue;
+    const int W = force_w ? wmax : (int)(TS < wcap ? TS : wcap);
+    long long kmax = 0;
+    const size_t lds = lds_for(W, &kmax);
+    if (lds > kMaxLds && S < CR) continue;
+    if (TS * (W + 1) > 0x7fffffffLL) return Plan{};  // step arithmetic must fit in int
+    pl.S = S;
+    pl.nrb = (int)nrb;
+    pl.rq = rq;
+    pl.rr = rr;
+    pl.W = W;
+    pl.kmax = (int)kmax;
+    pl.lds = lds;
+    pl.ws = S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1) : 0;
+    return pl;
+  }
+  return Plan{};  // no split fits (pl.S == 0): unsupported
 }
 
 hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t stream,
@@ -231,12 +272,13 @@ size_t workspace_bytes_for(int M, int N, int K, bool fused) {
 w4a16_status_t run_matmul(MatArgs a, bool fused, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
   const Plan pl = plan_gemm(a.M, a.N, a.K, fused);
-  if (pl.lds > kMaxLds) return W4A16_ERR_UNSUPPORTED;
+  if (pl.S == 0 || pl.lds > kMaxLds) return W4A16_ERR_UNSUPPORTED;
   if (workspace_bytes < pl.ws || (pl.ws > 0 && workspace == nullptr))
     return W4A16_ERR_INVALID_VALUE;
   if (pl.ws > 0 && !aligned(workspace, 16)) return W4A16_ERR_UNSUPPORTED;
-  a.rq = a.N / pl.nrb;
-  a.rr = a.N % pl.nrb;
+  a.rq = pl.rq;
+  a.rr = pl.rr;
+  a.kmax = pl.kmax;
   a.S = pl.S;
   a.CRS = (a.K >> 5) / pl.S;
   a.part = static_cast<float*>(workspace);
@@ -349,6 +391,15 @@ __attribute__((visibility("default"))) int w4a16_tuning_set(int enable, int mfma
   for (const KernEntry& e : kKernels)
     if (e.mfma == (mfma != 0) && e.lr == lr && e.D == D && e.LB == LB) return 1;
   return 0;
+}
+// Tuning builds only: the launch plan for a shape, as 12 ints
+// {mfma, lr, D, W, LB, nrb, S, rq, rr, kmax, lds, ws (bytes, clamped)}.
+__attribute__((visibility("default"))) void w4a16_tuning_plan(int M, int N, int K, int fused,
+                                                               long long* out) {
+  const Plan pl = plan_gemm(M, N, K, fused != 0);
+  const long long v[12] = {pl.mfma, pl.lr, pl.D, pl.W, pl.LB, pl.nrb, pl.S,
+                           pl.rq, pl.rr, pl.kmax, (long long)pl.lds, (long long)pl.ws};
+  for (int i = 0; i < 12; ++i) out[i] = v[i];
 }
 #endif
 #ifdef W4A16_TRACE

@@ -49,6 +49,9 @@ struct MatArgs {
   int rq, rr;
   int S, CRS;
   float* part;
+  // Segment slots per wave in the LDS area of partial sums (the most tasks
+  // one wave's step range can touch; see StreamSplit).
+  int kmax;
 };
 
 #define W4A16_DEV __device__ __forceinline__
@@ -90,6 +93,19 @@ W4A16_DEV uint16_t f32_to_bf16(float f) {
 }
 
 W4A16_DEV float silu(float v) { return v / (1.0f + expf(-v)); }
+
+// Word 3 of a gfx9 buffer descriptor for raw (untyped) dword access.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Reads the fp32 at g with a vector-memory (buffer) load.  Such a load is
+// counted with the weight loads, which complete in order, so it can be issued
+// right after the weight prologue without delaying any later scalar-memory or
+// LDS wait (a scalar load would).
+W4A16_DEV float load_f32_vmem(const float* g) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(g), (short)0, 4, kBufferWord3);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
+}
 
 // v + (v of another lane chosen by a DPP control; all lanes stay active)
 template <int CTRL>
@@ -201,15 +217,34 @@ W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[XMAX], const uint16_t*
 }
 
 // ---------------------------------------------------------------------------
+// Work split inside a workgroup (both matmul kernels).  The workgroup's rows
+// form ntasks tasks (row groups); a task is CPL chunk steps along K, so the
+// workgroup has TS = ntasks * CPL steps, step s = task * CPL + jj.  Wave w
+// executes the contiguous steps [begin(w), begin(w + 1)), begin(w) =
+// floor(w * TS / W): every wave gets the same number of steps to within one,
+// whatever the row count.  A wave sums each task it touches into a segment
+// partial, which it parks in LDS slot (w, task - first task of w), and notes
+// in LDS which wave starts (tw0) and which finishes (tw1) each task, and each
+// wave's first task (wft; a large value for a wave without steps).  After one
+// barrier the workgroup adds, for every task, the segments of waves tw0..tw1
+// in wave order (so results are reproducible bit for bit).
+// ---------------------------------------------------------------------------
+struct StreamSplit {
+  int TS, W, CPL;
+  W4A16_DEV int begin(int w) const { return (w * TS) / W; }
+  // the wave that executes step s: the w with begin(w) <= s < begin(w + 1)
+};
+constexpr int kNoTask = 1 << 30;
+
+// ---------------------------------------------------------------------------
 // VALU kernel, M = MT in {1, 2, 3}.
 //
-// Lane layout: a wave holds G = 64/L row slots of L lanes; lane (slot r,
-// position p) reads chunks p, p+L, p+2L, ... of its row (CR/L chunks), so the
+// Lane layout: a wave holds G = 64/L row slots of L lanes; at step (task, jj)
+// lane (slot r, position p) reads chunk p + L*jj of row r of the task, so the
 // L lanes of a row read L*16 contiguous bytes per load.  A task is one row
 // group (G rows; for the fused variant G/2 gate rows plus the same G/2 up
-// rows).  Workgroup b owns a contiguous row range; its waves take tasks
-// round-robin.  Each lane keeps D chunk loads in flight in a register ring
-// that runs across task boundaries.
+// rows) and takes CPL = CRS/L steps.  Each lane keeps D chunk loads in
+// flight in a register ring that runs across task boundaries.
 //
 // Per chunk and activation row: 16 bf16x2 dot products per 32 weights into
 // two block partials, then acc += partial * e4m3(scale).  x rows live in LDS
@@ -221,7 +256,10 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   W4A16_STAMP(t_start);
   extern __shared__ uint4 xs[];
   constexpr int G = 64 / L;
-  constexpr int RT = FUSED ? G / 2 : G;
+  constexpr int RT = FUSED ? G / 2 : G;   // output rows per task
+  constexpr int GL = L < 16 ? L : 16;     // lanes summed by DPP
+  constexpr int NSEG = L / GL;            // DPP groups per row slot
+  constexpr int V = G * MT;               // values in a segment partial: [slot][m]
   const int W = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -232,25 +270,32 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
   const int row_hi = row_lo + a.rq + (rb < a.rr ? 1 : 0);
   const int ntasks = (row_hi - row_lo + RT - 1) / RT;
+  const StreamSplit split{ntasks * CPL, W, CPL};
+  const int s_begin = split.begin(wv);
+  const int T = split.begin(wv + 1) - s_begin;  // steps of this wave (uniform)
+  const int ft = s_begin / CPL, jj0 = s_begin - ft * CPL;  // first task, its first step
   const int p = lane % L, r = lane / L;
   const int srow = FUSED ? (r % (G / 2)) : r;
   const bool is_up = FUSED && (r >= G / 2);
   const uint8_t* wq = is_up ? a.wq1 : a.wq0;
   const uint8_t* ws = is_up ? a.ws1 : a.ws0;
-  const int my_tasks = wv < ntasks ? (ntasks - 1 - wv) / W + 1 : 0;
-  const int T = my_tasks * CPL;  // chunk steps of this wave (uniform)
+  float* scr = reinterpret_cast<float*>(xs + MT * RSU) + wv * (G * MT * NSEG);
+  float* seg = reinterpret_cast<float*>(xs + MT * RSU) + W * (G * MT * NSEG);
+  int* tw0 = reinterpret_cast<int*>(seg + W * a.kmax * V);
+  int* tw1 = tw0 + W * a.kmax;
+  int* wft = tw1 + W * a.kmax;
 
   // ---- issue cursor: (task it_i, step jj_i) -> row pointers -------------
   const uint4* qp;
   const uint16_t* sp;
-  int s_i = 0, it_i = 0, jj_i = 0;
+  int s_i = 0, it_i = ft, jj_i = jj0;
   auto set_task = [&](int it) {
-    int row = row_lo + (wv + W * it) * RT + srow;
+    int row = row_lo + it * RT + srow;
     row = row < row_hi ? row : row_hi - 1;
     qp = reinterpret_cast<const uint4*>(wq + (size_t)row * (size_t)(K >> 1)) + c0 + p;
     sp = reinterpret_cast<const uint16_t*>(ws + (size_t)row * (size_t)(K >> 4)) + c0 + p;
   };
-  set_task(0);
+  set_task(it_i);
   uint4 qb[D];
   uint32_t sb[D];
   // load the current cursor position into slot d, then advance (the cursor
@@ -267,15 +312,25 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
       }
     }
   };
-  // x -> LDS (rows of K bf16; 16-byte units, swizzled): x loads first, then
-  // the weight prologue, then the LDS stores
+  // x -> LDS (rows of K bf16 in 16-byte units, swizzled): x loads first,
+  // then the weight prologue, then the LDS stores (loads complete in order,
+  // so the stores wait for x only)
   constexpr int XMAX = LB > 512 ? 8 : 16;
   uint4 xr[XMAX];
   auto xpos = [](int cu) { return xsw(cu >> 2, cu & 3); };
+#ifndef W4A16_WEIGHTS_FIRST
   x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, tid, blockDim.x);
+#endif
+  // (unconditional: a wave without steps loads its clamped start position)
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
   W4A16_STAMP(t_issued);
+  const float gv0 = load_f32_vmem(a.g0);
+  const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
+  if (lane == 0) wft[wv] = T > 0 ? ft : kNoTask;
+#ifdef W4A16_WEIGHTS_FIRST
+  x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, tid, blockDim.x);
+#endif
   x_stage_store(xs, xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, RSU, tid, blockDim.x, xpos);
   __syncthreads();
   W4A16_STAMP(t_barrier);
@@ -286,49 +341,31 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   float acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-  int it_c = 0, jj_c = 0;
+  int jj_c = jj0, kseg = 0;
 
-  // Task epilogue: sum each row slot's L lanes (DPP inside groups of up to 16
-  // lanes, then the NSEG group totals through a small per-wave LDS scratch),
-  // then one lane per output finishes it.
-  constexpr int GL = L < 16 ? L : 16;     // lanes summed by DPP
-  constexpr int NSEG = L / GL;            // groups per row slot
-  float* scr = reinterpret_cast<float*>(xs + MT * RSU) + wv * (G * MT * NSEG);
-  auto finish_task = [&]() {
-    const int seg = p / GL;
+  // Segment end: sum each row slot's L lanes (DPP inside groups of up to 16
+  // lanes, then the NSEG group totals through the per-wave LDS scratch) and
+  // park the slot totals [slot][m] in segment slot (wv, kseg).
+  auto finish_segment = [&](bool task_end) {
+    const int sg = p / GL;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const float v = group_allreduce<GL>(acc[m]);
-      if ((p % GL) == 0) scr[(r * MT + m) * NSEG + seg] = v;
+      if ((p % GL) == 0) scr[(r * MT + m) * NSEG + sg] = v;
       acc[m] = 0.0f;
     }
     wave_lds_sync();
-    const int base = row_lo + (wv + W * it_c) * RT;
-    // 1/g is read here, at the first use, so that no global load is waited
-    // for before the weight stream starts
-    const float ig0 = 1.0f / *a.g0;
-    const float ig1 = FUSED ? 1.0f / *a.g1 : 1.0f;
-    for (int o = lane; o < RT * MT; o += 64) {
-      const int rr = o / MT, m = o - rr * MT;   // output row (within task), activation row
-      float v = 0.0f, u = 0.0f;
+    if (lane < V) {
+      float v = 0.0f;
 #pragma unroll
-      for (int sg = 0; sg < NSEG; ++sg) v += scr[(rr * MT + m) * NSEG + sg];
-      if (FUSED) {
-#pragma unroll
-        for (int sg = 0; sg < NSEG; ++sg) u += scr[((rr + G / 2) * MT + m) * NSEG + sg];
-      }
-      const int row = base + rr;
-      if (row < row_hi) {
-        if (S > 1) {
-          a.part[((size_t)ks * a.M + m) * a.N + row] = v;
-          if (FUSED) a.part[((size_t)(S + ks) * a.M + m) * a.N + row] = u;
-        } else if (FUSED) {
-          a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v * ig0) * (u * ig1));
-        } else {
-          a.y[(size_t)m * a.N + row] = f32_to_bf16(v * ig0);
-        }
-      }
+      for (int i = 0; i < NSEG; ++i) v += scr[lane * NSEG + i];
+      seg[(wv * a.kmax + kseg) * V + lane] = v;
     }
+    if (lane == 0) {
+      if (kseg > 0 || jj0 == 0) tw0[ft + kseg] = wv;
+      if (task_end) tw1[ft + kseg] = wv;
+    }
+    ++kseg;
     wave_lds_sync();
   };
 
@@ -386,18 +423,52 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 #ifdef W4A16_TRACE
         if (t_first == 0) t_first = wall_clock64();
 #endif
-        if (++jj_c == CPL) {
-          finish_task();
-          jj_c = 0;
-          ++it_c;
-        }
+        const bool task_end = ++jj_c == CPL;
+        if (task_end || s0 + d + 1 == T) finish_segment(task_end);
+        if (task_end) jj_c = 0;
       }
       issue(d);
     }
   }
   W4A16_STAMP(t_end);
+
+  // ---- workgroup combine: output (row n, m) = sum of its task's segments --
+  __syncthreads();
+  const float ig0 = 1.0f / gv0;
+  const float ig1 = FUSED ? 1.0f / gv1 : 1.0f;
+  const int nrows = row_hi - row_lo;
+  for (int n = tid; n < nrows; n += blockDim.x) {
+    const int t = n / RT, rt = n - t * RT;
+    const int w0 = tw0[t], w1 = tw1[t];
+    float v[MT], u[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) v[m] = u[m] = 0.0f;
+    for (int w = w0; w <= w1; ++w) {
+      const int k = t - wft[w];
+      if (k < 0) continue;  // a wave without steps
+      const float* sg = seg + (w * a.kmax + k) * V;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        v[m] += sg[rt * MT + m];
+        if (FUSED) u[m] += sg[(rt + G / 2) * MT + m];
+      }
+    }
+    const int row = row_lo + n;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (S > 1) {
+        a.part[((size_t)ks * a.M + m) * a.N + row] = v[m];
+        if (FUSED) a.part[((size_t)(S + ks) * a.M + m) * a.N + row] = u[m];
+      } else if (FUSED) {
+        a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v[m] * ig0) * (u[m] * ig1));
+      } else {
+        a.y[(size_t)m * a.N + row] = f32_to_bf16(v[m] * ig0);
+      }
+    }
+  }
 #ifdef W4A16_TRACE
-  W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, (unsigned long long)T);
+  W4A16_STAMP(t_done);
+  W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);
 #endif
 }
 
@@ -413,10 +484,10 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 // (4 MFMAs per block, one FMA per result element).
 //
 // A task is R quads of weight rows (fused: R pairs of gate rows and the same
-// pairs of up rows).  Lane (beta, j) reads chunk beta, beta+16, ... of row j of
-// every quad (16 lanes x 16 B = 256 contiguous bytes per row per load) and,
-// once per chunk, the x slice of activation row 4*pp + j from LDS, which then
-// feeds the MFMAs of all R quads.
+// pairs of up rows) and takes CPL = ceil(CRS/16) steps.  At step (task, jj)
+// lane (beta, j) reads chunk beta + 16*jj of row j of every quad (16 lanes x
+// 16 B = 256 contiguous bytes per row per load) and the x slice of activation
+// row 4*pp + j from LDS, which then feeds the MFMAs of all R quads.
 // ---------------------------------------------------------------------------
 template <int P, int R, int D, bool FUSED, int LB>
 __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
@@ -424,6 +495,8 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   extern __shared__ uint4 xs[];
   constexpr int QS = FUSED ? 2 : 4;      // output rows per quad
   constexpr int RT = QS * R;             // output rows per task
+  constexpr int NA = R * P * 4;          // accumulators per lane
+  constexpr int V = NA * 4;              // values in a segment partial: [acc][j]
   const int W = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -434,28 +507,35 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
   const int row_hi = row_lo + a.rq + (rb < a.rr ? 1 : 0);
   const int ntasks = (row_hi - row_lo + RT - 1) / RT;
+  const StreamSplit split{ntasks * CPL, W, CPL};
+  const int s_begin = split.begin(wv);
+  const int T = split.begin(wv + 1) - s_begin;
+  const int ft = s_begin / CPL, jj0 = s_begin - ft * CPL;  // first task, its first step
   const int beta = lane >> 2, j = lane & 3;
   const int jr = FUSED ? (j & 1) : j;    // row within the quad
   const bool is_up = FUSED && (j >= 2);
   const uint8_t* wq = is_up ? a.wq1 : a.wq0;
   const uint8_t* ws = is_up ? a.ws1 : a.ws0;
-  const int my_tasks = wv < ntasks ? (ntasks - 1 - wv) / W + 1 : 0;
-  const int T = my_tasks * CPL;
   const bool ragged = (CRS & 15) != 0;
+  float* scr = reinterpret_cast<float*>(xs + 4 * P * RSU) + wv * (NA * 16);
+  float* seg = reinterpret_cast<float*>(xs + 4 * P * RSU) + W * (NA * 16);
+  int* tw0 = reinterpret_cast<int*>(seg + W * a.kmax * V);
+  int* tw1 = tw0 + W * a.kmax;
+  int* wft = tw1 + W * a.kmax;
 
   const uint4* qp[R];
   const uint16_t* sp[R];
-  int s_i = 0, it_i = 0, jj_i = 0;
+  int s_i = 0, it_i = ft, jj_i = jj0;
   auto set_task = [&](int it) {
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
-      int row = row_lo + (wv + W * it) * RT + rr * QS + jr;
+      int row = row_lo + it * RT + rr * QS + jr;
       row = row < row_hi ? row : row_hi - 1;
       qp[rr] = reinterpret_cast<const uint4*>(wq + (size_t)row * (size_t)(K >> 1)) + c0;
       sp[rr] = reinterpret_cast<const uint16_t*>(ws + (size_t)row * (size_t)(K >> 4)) + c0;
     }
   };
-  set_task(0);
+  set_task(it_i);
   uint4 qb[D][R];
   uint32_t sb[D][R];
   auto issue = [&](int d) {
@@ -475,14 +555,24 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
       }
     }
   };
-  // x -> LDS: rows 0..4P-1 (rows >= M are zero), 16 B pad per row
+  // x -> LDS: rows 0..4P-1 (rows >= M are zero), 16 B pad per row; x loads
+  // first, then the weight prologue, then the LDS stores
   constexpr int XMAX = LB > 512 ? 8 : 16;
   uint4 xr[XMAX];
   auto xpos = [](int cu) { return cu; };
+#ifndef W4A16_WEIGHTS_FIRST
   x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, tid, blockDim.x);
+#endif
+  // (unconditional: a wave without steps loads its clamped start position)
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
   W4A16_STAMP(t_issued);
+  const float gv0 = load_f32_vmem(a.g0);
+  const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
+  if (lane == 0) wft[wv] = T > 0 ? ft : kNoTask;
+#ifdef W4A16_WEIGHTS_FIRST
+  x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, tid, blockDim.x);
+#endif
   x_stage_store(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, RSU, tid, blockDim.x, xpos);
   __syncthreads();
   W4A16_STAMP(t_barrier);
@@ -497,15 +587,13 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
     for (int pp = 0; pp < P; ++pp)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[rr][pp][r] = 0.0f;
-  int it_c = 0, jj_c = 0;
+  int jj_c = jj0, kseg = 0;
 
-  // Task epilogue: for each of the V = R*P*4 accumulators, sum the 4 chunk
-  // columns inside each 16-lane row with DPP, park the 4 row totals per
-  // (value, weight row j) in a per-wave LDS scratch, then one lane per output
-  // adds them and finishes the output.
-  constexpr int V = R * P * 4;
-  float* scr = reinterpret_cast<float*>(xs + 4 * P * RSU) + wv * (V * 16);
-  auto finish_task = [&]() {
+  // Segment end: for each accumulator sum the 4 chunk columns inside each
+  // 16-lane row with DPP, park the 4 row totals per (accumulator, column j) in
+  // the per-wave scratch, then store their sums [acc][j] in segment slot
+  // (wv, kseg).  Accumulator index ai = (rr*P + pp)*4 + r = rr*4P + m.
+  auto finish_segment = [&](bool task_end) {
     const int row16 = lane >> 4;
 #pragma unroll
     for (int rr = 0; rr < R; ++rr)
@@ -516,37 +604,20 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
           float v = acc[rr][pp][r];
           v = dpp_add<kDppRor4>(v);
           v = dpp_add<kDppRor8>(v);
-          const int vi = (rr * P + pp) * 4 + r;
-          if ((lane & 12) == 0) scr[(vi * 4 + j) * 4 + row16] = v;
+          const int ai = (rr * P + pp) * 4 + r;
+          if ((lane & 12) == 0) scr[(ai * 4 + j) * 4 + row16] = v;
           acc[rr][pp][r] = 0.0f;
         }
     wave_lds_sync();
-    const int base = row_lo + (wv + W * it_c) * RT;
-    const float ig0 = 1.0f / *a.g0;       // read at the first use (see the VALU kernel)
-    const float ig1 = FUSED ? 1.0f / *a.g1 : 1.0f;
-    constexpr int NJ = FUSED ? 2 : 4;      // output rows per quad
-    for (int o = lane; o < V * NJ; o += 64) {
-      const int vi = o / NJ, jo = o - vi * NJ;
-      const int rr = vi / (P * 4), m = vi % (P * 4);
-      const float4 pv = *reinterpret_cast<const float4*>(&scr[(vi * 4 + jo) * 4]);
-      const float v = (pv.x + pv.y) + (pv.z + pv.w);
-      float u = 0.0f;
-      if (FUSED) {
-        const float4 pu = *reinterpret_cast<const float4*>(&scr[(vi * 4 + jo + 2) * 4]);
-        u = (pu.x + pu.y) + (pu.z + pu.w);
-      }
-      const int row = base + rr * QS + jo;
-      if (row < row_hi && m < a.M) {
-        if (S > 1) {
-          a.part[((size_t)ks * a.M + m) * a.N + row] = v;
-          if (FUSED) a.part[((size_t)(S + ks) * a.M + m) * a.N + row] = u;
-        } else if (FUSED) {
-          a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v * ig0) * (u * ig1));
-        } else {
-          a.y[(size_t)m * a.N + row] = f32_to_bf16(v * ig0);
-        }
-      }
+    for (int o = lane; o < V; o += 64) {
+      const float4 pv = *reinterpret_cast<const float4*>(&scr[o * 4]);
+      seg[(wv * a.kmax + kseg) * V + o] = (pv.x + pv.y) + (pv.z + pv.w);
     }
+    if (lane == 0) {
+      if (kseg > 0 || jj0 == 0) tw0[ft + kseg] = wv;
+      if (task_end) tw1[ft + kseg] = wv;
+    }
+    ++kseg;
     wave_lds_sync();
   };
 
@@ -602,18 +673,50 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
 #ifdef W4A16_TRACE
         if (t_first == 0) t_first = wall_clock64();
 #endif
-        if (++jj_c == CPL) {
-          finish_task();
-          jj_c = 0;
-          ++it_c;
-        }
+        const bool task_end = ++jj_c == CPL;
+        if (task_end || s0 + d + 1 == T) finish_segment(task_end);
+        if (task_end) jj_c = 0;
       }
       issue(d);
     }
   }
   W4A16_STAMP(t_end);
+
+  // ---- workgroup combine: output (row n, m) = sum of its task's segments --
+  __syncthreads();
+  const float ig0 = 1.0f / gv0;
+  const float ig1 = FUSED ? 1.0f / gv1 : 1.0f;
+  const int M = a.M;
+  const int nrows = row_hi - row_lo;
+  // item o = n * 4P + m (rows m >= M are skipped): a constant divisor
+  for (int o = tid; o < nrows * 4 * P; o += blockDim.x) {
+    const int n = o / (4 * P), m = o - n * (4 * P);
+    if (m >= M) continue;
+    const int t = n / RT, rt = n - t * RT;
+    const int rr = rt / QS, jo = rt - rr * QS;
+    const int idx = (rr * (4 * P) + m) * 4 + jo;  // [accumulator][column j]
+    const int w0 = tw0[t], w1 = tw1[t];
+    float v = 0.0f, u = 0.0f;
+    for (int w = w0; w <= w1; ++w) {
+      const int k = t - wft[w];
+      if (k < 0) continue;  // a wave without steps
+      const float* sg = seg + (w * a.kmax + k) * V;
+      v += sg[idx];
+      if (FUSED) u += sg[idx + 2];
+    }
+    const int row = row_lo + n;
+    if (S > 1) {
+      a.part[((size_t)ks * M + m) * a.N + row] = v;
+      if (FUSED) a.part[((size_t)(S + ks) * M + m) * a.N + row] = u;
+    } else if (FUSED) {
+      a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v * ig0) * (u * ig1));
+    } else {
+      a.y[(size_t)m * a.N + row] = f32_to_bf16(v * ig0);
+    }
+  }
 #ifdef W4A16_TRACE
-  W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, (unsigned long long)T);
+  W4A16_STAMP(t_done);
+  W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);
 #endif
 }
 
