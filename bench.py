@@ -115,11 +115,12 @@ def bench_square(args, dev, stream):
     wss = replicate(to_dev_u8(ws, dev), copies)
     gs = replicate(torch.tensor([g], dtype=torch.float32, device=dev), copies)
     y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+    work = w4.new_workspace(1, N, K, dev)   # zeroed once; every call leaves it zeroed
     bpc = weight_bytes(N, K)
 
     def step(strm):
         for i in range(copies):
-            w4.gemm(wqs[i], wss[i], gs[i], x, y=y, stream=strm)
+            w4.gemm(wqs[i], wss[i], gs[i], x, y=y, workspace=work, stream=strm)
 
     # eager reference (Python launches each call)
     step(stream)
@@ -160,6 +161,37 @@ def bench_square(args, dev, stream):
                 eager_gbs=bpc / t_eager / 1e9)
 
 
+def graph_time(fns, cycles, stream):
+    """Seconds per call of fns, captured once in a HIP graph (one call each)
+    and replayed `cycles` times after one untimed replay."""
+    import torch
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        for f in fns:
+            f(cap)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for f in fns:
+            f(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        graph.replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(cycles):
+            graph.replay()
+        end.record(stream)
+    end.synchronize()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e-3 / (cycles * len(fns))
+
+
 def bench_extra(dev, stream, cycles=10):
     import torch
     import block_scaled_fp4_w4a16_amd as w4
@@ -177,11 +209,11 @@ def bench_extra(dev, stream, cycles=10):
     for M in c["Ms"]:
         x = to_dev_bf16(synth.activations(c["seed_x"], M, K), dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        work = torch.empty(max(1, w4.workspace_size_gate_up(M, N, K)), dtype=torch.uint8, device=dev)
-        fns = [lambda i=i: w4.gemm_gate_up_swiglu(G[0][i], G[1][i], G[2][i], U[0][i], U[1][i],
-                                                  U[2][i], x, y=y, workspace=work, stream=stream)
+        work = w4.new_workspace(M, N, K, dev, fused=True)
+        fns = [lambda s, i=i: w4.gemm_gate_up_swiglu(G[0][i], G[1][i], G[2][i], U[0][i], U[1][i],
+                                                     U[2][i], x, y=y, workspace=work, stream=s)
                for i in range(copies)]
-        t = time_calls(fns, cycles, 1, stream)
+        t = graph_time(fns, cycles, stream)
         b = 2 * weight_bytes(N, K)
         out[f"gate_up_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
         log(f"[bench] gate_up M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
@@ -195,10 +227,10 @@ def bench_extra(dev, stream, cycles=10):
     for M in c["Ms"]:
         x = to_dev_bf16(synth.swiglu_activations(c["seed_a"], c["seed_b"], M, K), dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        work = torch.empty(max(1, w4.workspace_size(M, N, K)), dtype=torch.uint8, device=dev)
-        fns = [lambda i=i: w4.gemm(D[0][i], D[1][i], D[2][i], x, y=y, workspace=work, stream=stream)
+        work = w4.new_workspace(M, N, K, dev)
+        fns = [lambda s, i=i: w4.gemm(D[0][i], D[1][i], D[2][i], x, y=y, workspace=work, stream=s)
                for i in range(copies)]
-        t = time_calls(fns, cycles, 1, stream)
+        t = graph_time(fns, cycles, stream)
         b = weight_bytes(N, K)
         out[f"down_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
         log(f"[bench] down M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")

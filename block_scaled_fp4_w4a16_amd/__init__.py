@@ -20,7 +20,7 @@ import os
 import torch
 
 __all__ = ["gemm", "gemm_gate_up_swiglu", "dequant", "workspace_size",
-           "workspace_size_gate_up", "W4A16Error", "library_path", "lib", "MAX_M"]
+           "workspace_size_gate_up", "new_workspace", "W4A16Error", "library_path", "lib", "MAX_M"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libw4a16.so")
@@ -115,12 +115,22 @@ def _weights(wq, ws, g, name):
 
 
 def _workspace(workspace, need, device):
+    """The caller's workspace, or a fresh zero-filled one when the shape needs
+    one: split-K arrival counters sit at its start and must be zero before the
+    first call that uses it (every call leaves them zero again)."""
     if need == 0:
         return workspace, (workspace.numel() * workspace.element_size() if workspace is not None else 0)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=device)
     _check(workspace, "workspace", workspace.dtype, None)
     return workspace, workspace.numel() * workspace.element_size()
+
+
+def new_workspace(M: int, N: int, K: int, device, fused: bool = False):
+    """A zero-filled workspace for (M, N, K) (at least 16 bytes), reusable by
+    any number of calls of that shape made one after another."""
+    need = (workspace_size_gate_up if fused else workspace_size)(M, N, K)
+    return torch.zeros(max(need, 16), dtype=torch.uint8, device=device)
 
 
 def gemm(wq, ws, g, x, y=None, workspace=None, stream=None):

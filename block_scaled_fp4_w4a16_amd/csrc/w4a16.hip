@@ -29,7 +29,16 @@ int cu_count() {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-constexpr size_t kMaxLds = 160 * 1024;
+// Dynamic LDS limit per workgroup (160 KiB per CU, less a little for the
+// kernels' static LDS).
+constexpr size_t kMaxLds = 160 * 1024 - 256;
+
+// The split-K arrival counters (one int per row block) occupy a fixed area at
+// the front of the workspace, the same for every shape, so that calls of
+// different shapes can share one workspace: no call's partials ever overlap
+// another call's counters.  The fp32 partials follow it.
+constexpr size_t kCounterBytes = 4096;
+constexpr int kMaxSplitRowBlocks = (int)(kCounterBytes / sizeof(int));
 
 // How one matmul call is launched.
 struct Plan {
@@ -193,6 +202,7 @@ Plan plan_gemm(int M, int N, int K, bool fused) {
 #endif
     if (nrb > groups) nrb = groups;
     if (nrb > N) nrb = N;
+    if (S > 1 && nrb > kMaxSplitRowBlocks) nrb = kMaxSplitRowBlocks;
     const int rq = N / (int)nrb, rr = N % (int)nrb;
     const long long ntasks = ((long long)rq + (rr > 0) + RT - 1) / RT;  // tasks of the largest block
     const int CPL = pl.mfma ? (CRS + 15) / 16 : CRS / pl.lr;
@@ -224,7 +234,9 @@ Plan plan_gemm(int M, int N, int K, bool fused) {
     pl.W = W;
     pl.kmax = (int)kmax;
     pl.lds = lds;
-    pl.ws = S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1) : 0;
+    pl.ws = S > 1 ? kCounterBytes +
+                        (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1)
+                  : 0;
     return pl;
   }
   return Plan{};  // no split fits (pl.S == 0): unsupported
@@ -247,14 +259,7 @@ hipError_t dispatch(const Plan& pl, bool fused, hipStream_t s, const MatArgs& a)
   const KernEntry* k = find_kernel(pl.mfma, rows, pl.lr, pl.D, fused, pl.LB);
   if (!k || pl.W * 64 > pl.LB) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)pl.nrb, (unsigned)pl.S), block((unsigned)(pl.W * 64));
-  hipError_t e = launch(k->fn, grid, block, pl.lds, s, a);
-  if (e != hipSuccess || pl.S == 1) return e;
-  const long long MN = (long long)a.M * a.N;
-  long long nb = (MN + 255) / 256;
-  if (nb > 4LL * cu_count()) nb = 4LL * cu_count();
-  const void* comb = fused ? reinterpret_cast<const void*>(&k_combine<true>)
-                           : reinterpret_cast<const void*>(&k_combine<false>);
-  return launch(comb, dim3((unsigned)nb), dim3(256), 0, s, a);
+  return launch(k->fn, grid, block, pl.lds, s, a);
 }
 
 w4a16_status_t check_shape(int M, int N, int K) {
@@ -281,7 +286,8 @@ w4a16_status_t run_matmul(MatArgs a, bool fused, void* workspace, size_t workspa
   a.kmax = pl.kmax;
   a.S = pl.S;
   a.CRS = (a.K >> 5) / pl.S;
-  a.part = static_cast<float*>(workspace);
+  a.cnt = static_cast<int*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
   const hipError_t e = dispatch(pl, fused, stream, a);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }

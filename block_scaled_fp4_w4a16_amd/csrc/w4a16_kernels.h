@@ -45,10 +45,12 @@ struct MatArgs {
   // blockIdx.y covers chunks [ks*CRS, (ks+1)*CRS) of every row (a chunk is
   // 32 inputs).  With S > 1 the workgroup writes fp32 partial sums
   // part[ks][M][N] (fused: gate partials, then up partials at part + S*M*N)
-  // instead of y, and k_combine finishes them.
+  // instead of y, and the last workgroup of the row block to finish adds
+  // them (splitk_finish); cnt[rb] counts the arrivals.
   int rq, rr;
   int S, CRS;
   float* part;
+  int* cnt;
   // Segment slots per wave in the LDS area of partial sums (the most tasks
   // one wave's step range can touch; see StreamSplit).
   int kmax;
@@ -214,6 +216,56 @@ W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[XMAX], const uint16_t*
   for (; c.m < rows; c.advance(nthr, upr))
     xs[c.m * RSU + pos(c.cu)] =
         c.m < M ? xg[(size_t)c.m * (K >> 3) + u0 + c.cu] : make_uint4(0u, 0u, 0u, 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K completion inside the matmul kernel (no second launch).  Every
+// workgroup (rb, ks) stores its fp32 partials part[ks][m][row] for the rows
+// [row_lo, row_lo + nrows) of its row block with agent-scope stores, which
+// write through to the device's point of coherence (the L2 of each XCD is
+// not coherent with the others'), waits until they have completed, and then
+// thread 0 adds one to cnt[rb] with a relaxed agent-scope atomic.  The
+// workgroup that sees S - 1 arrivals before its own is the last one: it
+// reads every slice's partials with agent-scope loads, adds them in slice
+// order 0..S-1 (a fixed order, so results do not depend on which slice
+// finished last), writes y, and sets cnt[rb] back to zero for the next call.
+// Each counter sees S atomics per call, no cache-wide write-back or
+// invalidation is needed, and nothing ever waits for another workgroup.
+// ---------------------------------------------------------------------------
+W4A16_DEV void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+W4A16_DEV float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <bool FUSED>
+W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, float ig0,
+                             float ig1) {
+  __shared__ int is_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+  __syncthreads();                // ... and so have every other wave's
+  if (threadIdx.x == 0) {
+    const int before = __hip_atomic_fetch_add(a.cnt + rb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = before == a.S - 1;
+    if (is_last) __hip_atomic_store(a.cnt + rb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  const size_t MN = (size_t)a.M * a.N;
+  for (int o = threadIdx.x; o < nrows * a.M; o += blockDim.x) {
+    const int m = o / nrows, n = o - m * nrows;   // consecutive threads: consecutive rows
+    const size_t i = (size_t)m * a.N + row_lo + n;
+    float v = 0.0f;
+    for (int s = 0; s < a.S; ++s) v += load_coherent(a.part + (size_t)s * MN + i);
+    if (FUSED) {
+      float u = 0.0f;
+      for (int s = 0; s < a.S; ++s) u += load_coherent(a.part + (size_t)(a.S + s) * MN + i);
+      a.y[i] = f32_to_bf16(silu(v * ig0) * (u * ig1));
+    } else {
+      a.y[i] = f32_to_bf16(v * ig0);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -457,8 +509,8 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (S > 1) {
-        a.part[((size_t)ks * a.M + m) * a.N + row] = v[m];
-        if (FUSED) a.part[((size_t)(S + ks) * a.M + m) * a.N + row] = u[m];
+        store_coherent(a.part + ((size_t)ks * a.M + m) * a.N + row, v[m]);
+        if (FUSED) store_coherent(a.part + ((size_t)(S + ks) * a.M + m) * a.N + row, u[m]);
       } else if (FUSED) {
         a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v[m] * ig0) * (u[m] * ig1));
       } else {
@@ -466,6 +518,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
       }
     }
   }
+  if (S > 1) splitk_finish<FUSED>(a, rb, row_lo, row_hi - row_lo, ig0, ig1);
 #ifdef W4A16_TRACE
   W4A16_STAMP(t_done);
   W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);
@@ -706,42 +759,19 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
     }
     const int row = row_lo + n;
     if (S > 1) {
-      a.part[((size_t)ks * M + m) * a.N + row] = v;
-      if (FUSED) a.part[((size_t)(S + ks) * M + m) * a.N + row] = u;
+      store_coherent(a.part + ((size_t)ks * M + m) * a.N + row, v);
+      if (FUSED) store_coherent(a.part + ((size_t)(S + ks) * M + m) * a.N + row, u);
     } else if (FUSED) {
       a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v * ig0) * (u * ig1));
     } else {
       a.y[(size_t)m * a.N + row] = f32_to_bf16(v * ig0);
     }
   }
+  if (S > 1) splitk_finish<FUSED>(a, rb, row_lo, row_hi - row_lo, ig0, ig1);
 #ifdef W4A16_TRACE
   W4A16_STAMP(t_done);
   W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);
 #endif
-}
-
-// ---------------------------------------------------------------------------
-// Split-K epilogue: y[m][n] = f(sum over s = 0..S-1 of part[s][m][n]) in that
-// fixed order (bitwise reproducible).  f = bf16(v / g), or for the fused
-// variant bf16(silu(gate / g_gate) * (up / g_up)).
-// ---------------------------------------------------------------------------
-template <bool FUSED>
-__global__ void __launch_bounds__(256) k_combine(MatArgs a) {
-  const long long MN = (long long)a.M * a.N;
-  const float ig0 = 1.0f / *a.g0;
-  const float ig1 = FUSED ? 1.0f / *a.g1 : 1.0f;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < MN;
-       i += (long long)gridDim.x * blockDim.x) {
-    float v = 0.0f;
-    for (int s = 0; s < a.S; ++s) v += a.part[(size_t)s * MN + i];
-    if (FUSED) {
-      float u = 0.0f;
-      for (int s = 0; s < a.S; ++s) u += a.part[(size_t)(a.S + s) * MN + i];
-      a.y[i] = f32_to_bf16(silu(v * ig0) * (u * ig1));
-    } else {
-      a.y[i] = f32_to_bf16(v * ig0);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------

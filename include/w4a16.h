@@ -66,10 +66,16 @@ typedef enum {
  *   workspace : device scratch of at least w4a16_workspace_size(M, N, K)
  *               bytes, 16-byte aligned (may be NULL when that size is 0).
  *               When the x slice a workgroup needs does not fit in LDS
- *               (M * K large) or N is small, the reduction is split over K:
- *               each K-slice writes fp32 partial sums here and a second
- *               kernel adds them in a fixed order.  Its contents need no
- *               initialisation and are garbage after the call.
+ *               (M * K large) the reduction is split over K: each K-slice
+ *               writes fp32 partial sums here, and the last workgroup of
+ *               each row block to finish adds them in a fixed slice order,
+ *               in the same kernel.  The first 4096 bytes of such a
+ *               workspace hold the arrival counters of the row blocks: they
+ *               must be ZERO BEFORE THE FIRST CALL that uses the workspace
+ *               (one hipMemset after allocation), and every call leaves them
+ *               zero again, so one zero-fill serves any number of calls, of
+ *               any shapes, made one after another.  The partial sums after
+ *               them need no initialisation.
  * Accuracy contract: |y - y_exact| <= 1e-2 * sum_k |x[m][k] * W[n][k]| + 1e-6
  * for every (m, n).  Defined by the page's schema and "NVFP4 W4A16" format
  * (FlashRT, "Qwen3.6-27B NVFP4 on RTX 5090", section 1).
@@ -104,7 +110,8 @@ w4a16_status_t w4a16_gemm_gate_up_swiglu(const uint8_t* wq_gate, const uint8_t* 
 w4a16_status_t w4a16_dequant(const uint8_t* wq, const uint8_t* ws, const float* g, float* w,
                              int N, int K, hipStream_t stream);
 
-/* Bytes of workspace w4a16_gemm needs for this shape (0 = none). */
+/* Bytes of workspace w4a16_gemm needs for this shape (0 = none, or an
+ * unsupported shape). */
 size_t w4a16_workspace_size(int M, int N, int K);
 
 /* Bytes of workspace w4a16_gemm_gate_up_swiglu needs for this shape. */
@@ -114,7 +121,7 @@ size_t w4a16_workspace_size_gate_up(int M, int N, int K);
 const char* w4a16_status_string(w4a16_status_t status);
 
 /* ABI version of this header: bumped on any incompatible change. */
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
 int w4a16_abi_version(void);
 
 #ifdef __cplusplus

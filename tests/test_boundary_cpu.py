@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.w4a16_abi_version() == 1
+    assert lib.w4a16_abi_version() == 2
     for st in (0, 1, 2, 3):
         assert len(w4.status_string(st)) > 0
     assert w4.status_string(99) == "unknown status"
@@ -90,10 +90,13 @@ def test_workspace_sizes(lib):
     # small x: no split, no workspace
     assert w4.workspace_size(1, 5120, 5120) == 0
     assert w4.workspace_size_gate_up(7, 17408, 5120) == 0
-    # 8 rows of a 17408-wide x do not fit in LDS: K is split in two
-    assert w4.workspace_size(7, 5120, 17408) == 2 * 7 * 5120 * 4
-    assert w4.workspace_size(8, 5120, 17408) == 2 * 8 * 5120 * 4
-    assert w4.workspace_size_gate_up(8, 512, 17408) == 2 * 2 * 8 * 512 * 4
+    # 8 rows of a 17408-wide x do not fit in LDS: K is split; the workspace
+    # holds the row-block arrival counters (a fixed 4096 bytes) and the fp32
+    # partials of every slice
+    for M, N, K, fused in [(7, 5120, 17408, False), (8, 5120, 17408, False), (8, 512, 17408, True)]:
+        size = (w4.workspace_size_gate_up if fused else w4.workspace_size)(M, N, K)
+        S, counters = divmod(size - 4096, M * N * 4 * (2 if fused else 1))
+        assert S >= 2 and counters == 0, (M, N, K, size)
     assert w4.workspace_size(17, 64, 256) == 0            # unsupported shape: 0
 
 

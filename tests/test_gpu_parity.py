@@ -298,12 +298,46 @@ def test_split_k_workspace_is_required_and_used():
     st = lib.w4a16_gemm(dwq.data_ptr(), dws.data_ptr(), dg.data_ptr(), dx.data_ptr(), y.data_ptr(),
                         M, N, K, None, 0, None)
     assert st == w4.ERR_INVALID_VALUE
-    # workspace full of garbage: results must not depend on its contents
-    work = torch.full((w4.workspace_size(M, N, K),), 0x7F, dtype=torch.uint8, device="cuda")
+    # the arrival counters at the start must be zero; the fp32 partials after
+    # them need no initialisation: fill everything past the first 4 KiB (the
+    # counter area) with garbage
+    size = w4.workspace_size(M, N, K)
+    work = torch.zeros((size,), dtype=torch.uint8, device="cuda")
+    work[4096:] = 0x7F
     y = w4.gemm(dwq, dws, dg, dx, workspace=work)
     torch.cuda.synchronize()
     ref, a = oracle.gemm(wq, ws, g, x, M, N, K, nthreads=NTHREADS)
-    report_and_check(h_bf16(y), ref, oracle.gemm_bound(a), "split-K garbage workspace")
+    report_and_check(h_bf16(y), ref, oracle.gemm_bound(a), "split-K garbage partials")
+    # every call leaves the counters (the first 4096 bytes) zero
+    assert int(work[:4096].count_nonzero()) == 0
+
+
+def test_split_k_workspace_reused_by_many_calls():
+    # one zero-fill, then split and unsplit calls of several shapes back to
+    # back on one workspace, each checked against the oracle, twice
+    work = torch.zeros((1 << 22,), dtype=torch.uint8, device="cuda")
+    cases = [(8, 640, 17408, False), (5, 1003, 17408, False), (16, 96, 33024, False),
+             (7, 5120, 17408, False), (6, 200, 17408, True), (2, 640, 17408, False)]
+    for i, (M, N, K, fused) in enumerate(cases):
+        need = (w4.workspace_size_gate_up if fused else w4.workspace_size)(M, N, K)
+        assert need <= work.numel()
+        wq, ws, g = weights(50 + i, N, K)
+        x = synth.activations(60 + i, M, K)
+        for rep in range(2):
+            if fused:
+                y = w4.gemm_gate_up_swiglu(d_u8(wq), d_u8(ws), d_g(g), d_u8(wq), d_u8(ws), d_g(g),
+                                           d_bf16(x), workspace=work)
+            else:
+                y = w4.gemm(d_u8(wq), d_u8(ws), d_g(g), d_bf16(x), workspace=work)
+            torch.cuda.synchronize()
+            if fused:
+                r = oracle.gate_up_swiglu(wq, ws, g, wq, ws, g, x, M, N, K, nthreads=NTHREADS)
+                report_and_check(h_bf16(y), r["y"], oracle.swiglu_bound(r["gate"], r["up"], r["a_gate"],
+                                                                          r["a_up"]), f"reuse fused {i}")
+            else:
+                ref, a = oracle.gemm(wq, ws, g, x, M, N, K, nthreads=NTHREADS)
+                report_and_check(h_bf16(y), ref, oracle.gemm_bound(a), f"reuse {M}x{N}x{K} #{rep}")
+    assert int(work[:4096].count_nonzero()) == 0
 
 
 def test_graph_capture_replays_match_eager():
@@ -312,7 +346,7 @@ def test_graph_capture_replays_match_eager():
         wq, ws, g = weights(22, N, K)
         dwq, dws, dg = d_u8(wq), d_u8(ws), d_g(g)
         dx = d_bf16(synth.activations(23, M, K))
-        work = torch.empty(max(1, w4.workspace_size(M, N, K)), dtype=torch.uint8, device="cuda")
+        work = w4.new_workspace(M, N, K, "cuda")
         eager = w4.gemm(dwq, dws, dg, dx, workspace=work).clone()
         y = torch.empty_like(eager)
         s = torch.cuda.Stream()
