@@ -166,39 +166,44 @@ W4A16_DEV void wave_lds_sync() {
 W4A16_DEV int xsw(int c, int q) { return 4 * c + (q ^ (((c >> 1) ^ (c >> 2)) & 3)); }
 
 // Stage `rows` rows of x (K bf16 each; rows >= M are zero) into LDS units
-// xs[m*RSU + pos(cu)].  Phase 1 loads the first XMAX units per thread into
+// xs[m*RSU + pos(cu)].  The slice is `upr` 16-byte units per row starting at
+// unit u0 of each x row (a row of x has K/8 units); unit u of the staged
+// block is (row u / upr, column u % upr), and thread tid handles units tid,
+// tid + nthr, ...  Phase 1 loads the first XMAX units per thread into
 // registers *before* the caller issues its weight prologue, so that storing
-// them (phase 2) waits only for x, since loads complete in order; units beyond
-// XMAX per thread (only for very wide x) are staged after the prologue.
-// The slice is `upr` units per row starting at unit u0 of each x row (a row
-// of x has K/8 units); unit u of the staged block is (row u / upr, column
-// u % upr).  Thread tid handles units tid, tid + nthr, ...; the (row, column)
-// pair is advanced incrementally (no division per unit).
-struct XCursor {
-  int m, cu;
-  W4A16_DEV void init(int tid, int upr) {
-    m = tid / upr;
-    cu = tid - m * upr;
-  }
-  W4A16_DEV void advance(int nthr, int upr) {
-    cu += nthr;
-    while (cu >= upr) {
-      cu -= upr;
-      ++m;
-    }
+// them (phase 2) waits only for x, since loads complete in order; units
+// beyond XMAX per thread (only for very wide x) are staged after the
+// prologue.  The code is straight-line: it runs at the start of every
+// launch, when the instruction cache is cold, so it has no loops and only
+// wave-uniform guards and short lane-masked loads.
+struct XUnits {
+  int total, upr;
+  float rinv;  // ~1/upr
+  W4A16_DEV XUnits(int rows, int upr_) : total(rows * upr_), upr(upr_), rinv(1.0f / (float)upr_) {}
+  // (row, column) of unit u: the float quotient is off by at most one for
+  // the unit counts used here (u < 2^22), and one correction step fixes it
+  W4A16_DEV void split(int u, int& m, int& cu) const {
+    int q = (int)((float)u * rinv);
+    int r = u - q * upr;
+    q = r < 0 ? q - 1 : (r >= upr ? q + 1 : q);
+    m = q;
+    cu = u - q * upr;
   }
 };
 template <int XMAX>
 W4A16_DEV void x_stage_issue(uint4 (&xr)[XMAX], const uint16_t* x, int M, int rows, int K,
                              int u0, int upr, int tid, int nthr) {
   const uint4* xg = reinterpret_cast<const uint4*>(x);
-  XCursor c;
-  c.init(tid, upr);
+  const XUnits xu(rows, upr);
 #pragma unroll
   for (int i = 0; i < XMAX; ++i) {
-    xr[i] = (c.m < rows && c.m < M) ? xg[(size_t)c.m * (K >> 3) + u0 + c.cu]
-                                    : make_uint4(0u, 0u, 0u, 0u);
-    c.advance(nthr, upr);
+    xr[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (i * nthr < xu.total) {          // wave-uniform
+      const int u = tid + i * nthr;
+      int m, cu;
+      xu.split(u, m, cu);
+      if (u < xu.total && m < M) xr[i] = xg[(size_t)m * (K >> 3) + u0 + cu];
+    }
   }
 }
 template <int XMAX, typename Pos>
@@ -206,16 +211,21 @@ W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[XMAX], const uint16_t*
                              int rows, int K, int u0, int upr, int RSU, int tid, int nthr,
                              Pos pos) {
   const uint4* xg = reinterpret_cast<const uint4*>(x);
-  XCursor c;
-  c.init(tid, upr);
+  const XUnits xu(rows, upr);
 #pragma unroll
   for (int i = 0; i < XMAX; ++i) {
-    if (c.m < rows) xs[c.m * RSU + pos(c.cu)] = xr[i];
-    c.advance(nthr, upr);
+    if (i * nthr < xu.total) {
+      const int u = tid + i * nthr;
+      int m, cu;
+      xu.split(u, m, cu);
+      if (u < xu.total) xs[m * RSU + pos(cu)] = xr[i];
+    }
   }
-  for (; c.m < rows; c.advance(nthr, upr))
-    xs[c.m * RSU + pos(c.cu)] =
-        c.m < M ? xg[(size_t)c.m * (K >> 3) + u0 + c.cu] : make_uint4(0u, 0u, 0u, 0u);
+  for (int u = tid + XMAX * nthr; u < xu.total; u += nthr) {
+    int m, cu;
+    xu.split(u, m, cu);
+    xs[m * RSU + pos(cu)] = m < M ? xg[(size_t)m * (K >> 3) + u0 + cu] : make_uint4(0u, 0u, 0u, 0u);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -364,18 +374,25 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
       }
     }
   };
-  // x -> LDS (rows of K bf16 in 16-byte units, swizzled): x loads first,
-  // then the weight prologue, then the LDS stores (loads complete in order,
-  // so the stores wait for x only)
+  // x -> LDS (rows of K bf16 in 16-byte units, swizzled): ring slot 0, the
+  // x loads, the rest of the weight prologue, then the LDS stores (loads
+  // complete in order, so the stores wait for slot 0 and x only)
   constexpr int XMAX = LB > 512 ? 8 : 16;
   uint4 xr[XMAX];
   auto xpos = [](int cu) { return xsw(cu >> 2, cu & 3); };
 #ifndef W4A16_WEIGHTS_FIRST
+  // ring slot 0 first: the weight stream starts as early in the (cold)
+  // instruction stream as possible, and the first step needs it anyway
+  issue(0);
   x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, tid, blockDim.x);
-#endif
-  // (unconditional: a wave without steps loads its clamped start position)
+#pragma unroll
+  for (int d = 1; d < D; ++d) issue(d);
+#else
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
+#endif
+  // (issue is unconditional: a wave without steps loads its clamped start
+  // position)
   W4A16_STAMP(t_issued);
   const float gv0 = load_f32_vmem(a.g0);
   const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
@@ -608,17 +625,24 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
       }
     }
   };
-  // x -> LDS: rows 0..4P-1 (rows >= M are zero), 16 B pad per row; x loads
-  // first, then the weight prologue, then the LDS stores
+  // x -> LDS: rows 0..4P-1 (rows >= M are zero), 16 B pad per row; ring
+  // slot 0, the x loads, the rest of the weight prologue, then the LDS stores
   constexpr int XMAX = LB > 512 ? 8 : 16;
   uint4 xr[XMAX];
   auto xpos = [](int cu) { return cu; };
 #ifndef W4A16_WEIGHTS_FIRST
+  // ring slot 0 first: the weight stream starts as early in the (cold)
+  // instruction stream as possible, and the first step needs it anyway
+  issue(0);
   x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, tid, blockDim.x);
-#endif
-  // (unconditional: a wave without steps loads its clamped start position)
+#pragma unroll
+  for (int d = 1; d < D; ++d) issue(d);
+#else
 #pragma unroll
   for (int d = 0; d < D; ++d) issue(d);
+#endif
+  // (issue is unconditional: a wave without steps loads its clamped start
+  // position)
   W4A16_STAMP(t_issued);
   const float gv0 = load_f32_vmem(a.g0);
   const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
