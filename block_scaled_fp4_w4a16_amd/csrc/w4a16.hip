@@ -226,7 +226,9 @@ Plan plan_gemm(int M, int N, int K, bool fused) {
     long long kmax = 0;
     const size_t lds = lds_for(W, &kmax);
     if (lds > kMaxLds && S < CR) continue;
-    if (TS * (W + 1) > 0x7fffffffLL) return Plan{};  // step arithmetic must fit in int
+    // quotients in the kernels (div_small) are exact below 2^23
+    if (TS * (W + 1) >= (1LL << 23) || (long long)xrows * CRS * 4 + 1024LL * 16 >= (1LL << 23))
+      return Plan{};
     pl.S = S;
     pl.nrb = (int)nrb;
     pl.rq = rq;
@@ -286,6 +288,10 @@ w4a16_status_t run_matmul(MatArgs a, bool fused, void* workspace, size_t workspa
   a.kmax = pl.kmax;
   a.S = pl.S;
   a.CRS = (a.K >> 5) / pl.S;
+  const int cpl = pl.mfma ? (a.CRS + 15) / 16 : a.CRS / pl.lr;
+  a.rW = 1.0f / (float)pl.W;
+  a.rCPL = 1.0f / (float)cpl;
+  a.rUPR = 1.0f / (float)(a.CRS * 4);
   a.cnt = static_cast<int*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
   const hipError_t e = dispatch(pl, fused, stream, a);

@@ -54,9 +54,23 @@ struct MatArgs {
   // Segment slots per wave in the LDS area of partial sums (the most tasks
   // one wave's step range can touch; see StreamSplit).
   int kmax;
+  // fp32 reciprocals of the launch's divisors (waves per workgroup, chunk
+  // steps per task, x units per row), for div_small
+  float rW, rCPL, rUPR;
 };
 
 #define W4A16_DEV __device__ __forceinline__
+
+// floor(x / d) for 0 <= x < 2^23 and d >= 1, given r = fp32(1/d): the float
+// quotient is off by at most one, and one correction step makes it exact.
+// Integer division proper costs ~25 instructions; the kernels' prologues run
+// with a cold instruction cache, so short code there is worth having.
+W4A16_DEV int div_small(int x, int d, float r) {
+  const int q = (int)((float)x * r);
+  const int rem = x - q * d;
+  return rem < 0 ? q - 1 : (rem >= d ? q + 1 : q);
+}
+
 
 // two E2M1 codes (byte B of w) -> two bf16 in one dword (low half = low nibble)
 template <int B>
@@ -178,23 +192,19 @@ W4A16_DEV int xsw(int c, int q) { return 4 * c + (q ^ (((c >> 1) ^ (c >> 2)) & 3
 // wave-uniform guards and short lane-masked loads.
 struct XUnits {
   int total, upr;
-  float rinv;  // ~1/upr
-  W4A16_DEV XUnits(int rows, int upr_) : total(rows * upr_), upr(upr_), rinv(1.0f / (float)upr_) {}
-  // (row, column) of unit u: the float quotient is off by at most one for
-  // the unit counts used here (u < 2^22), and one correction step fixes it
+  float rinv;  // fp32(1/upr)
+  W4A16_DEV XUnits(int rows, int upr_, float rinv_) : total(rows * upr_), upr(upr_), rinv(rinv_) {}
+  // (row, column) of unit u
   W4A16_DEV void split(int u, int& m, int& cu) const {
-    int q = (int)((float)u * rinv);
-    int r = u - q * upr;
-    q = r < 0 ? q - 1 : (r >= upr ? q + 1 : q);
-    m = q;
-    cu = u - q * upr;
+    m = div_small(u, upr, rinv);
+    cu = u - m * upr;
   }
 };
 template <int XMAX>
 W4A16_DEV void x_stage_issue(uint4 (&xr)[XMAX], const uint16_t* x, int M, int rows, int K,
-                             int u0, int upr, int tid, int nthr) {
+                             int u0, int upr, float rupr, int tid, int nthr) {
   const uint4* xg = reinterpret_cast<const uint4*>(x);
-  const XUnits xu(rows, upr);
+  const XUnits xu(rows, upr, rupr);
 #pragma unroll
   for (int i = 0; i < XMAX; ++i) {
     xr[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -208,10 +218,10 @@ W4A16_DEV void x_stage_issue(uint4 (&xr)[XMAX], const uint16_t* x, int M, int ro
 }
 template <int XMAX, typename Pos>
 W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[XMAX], const uint16_t* x, int M,
-                             int rows, int K, int u0, int upr, int RSU, int tid, int nthr,
-                             Pos pos) {
+                             int rows, int K, int u0, int upr, float rupr, int RSU, int tid,
+                             int nthr, Pos pos) {
   const uint4* xg = reinterpret_cast<const uint4*>(x);
-  const XUnits xu(rows, upr);
+  const XUnits xu(rows, upr, rupr);
 #pragma unroll
   for (int i = 0; i < XMAX; ++i) {
     if (i * nthr < xu.total) {
@@ -292,9 +302,9 @@ W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, fl
 // in wave order (so results are reproducible bit for bit).
 // ---------------------------------------------------------------------------
 struct StreamSplit {
-  int TS, W, CPL;
-  W4A16_DEV int begin(int w) const { return (w * TS) / W; }
-  // the wave that executes step s: the w with begin(w) <= s < begin(w + 1)
+  int TS, W;
+  float rW;
+  W4A16_DEV int begin(int w) const { return div_small(w * TS, W, rW); }
 };
 constexpr int kNoTask = 1 << 30;
 
@@ -322,7 +332,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   constexpr int GL = L < 16 ? L : 16;     // lanes summed by DPP
   constexpr int NSEG = L / GL;            // DPP groups per row slot
   constexpr int V = G * MT;               // values in a segment partial: [slot][m]
-  const int W = blockDim.x >> 6;
+  const int W = blockDim.x >> 6, NT = blockDim.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.K, S = a.S, CRS = a.CRS;  // CRS: chunks per row in this K-slice
@@ -332,10 +342,10 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
   const int row_hi = row_lo + a.rq + (rb < a.rr ? 1 : 0);
   const int ntasks = (row_hi - row_lo + RT - 1) / RT;
-  const StreamSplit split{ntasks * CPL, W, CPL};
+  const StreamSplit split{ntasks * CPL, W, a.rW};
   const int s_begin = split.begin(wv);
   const int T = split.begin(wv + 1) - s_begin;  // steps of this wave (uniform)
-  const int ft = s_begin / CPL, jj0 = s_begin - ft * CPL;  // first task, its first step
+  const int ft = div_small(s_begin, CPL, a.rCPL), jj0 = s_begin - ft * CPL;  // first task, its first step
   const int p = lane % L, r = lane / L;
   const int srow = FUSED ? (r % (G / 2)) : r;
   const bool is_up = FUSED && (r >= G / 2);
@@ -384,7 +394,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   // ring slot 0 first: the weight stream starts as early in the (cold)
   // instruction stream as possible, and the first step needs it anyway
   issue(0);
-  x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, tid, blockDim.x);
+  x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
 #pragma unroll
   for (int d = 1; d < D; ++d) issue(d);
 #else
@@ -398,9 +408,9 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
   if (lane == 0) wft[wv] = T > 0 ? ft : kNoTask;
 #ifdef W4A16_WEIGHTS_FIRST
-  x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, tid, blockDim.x);
+  x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
 #endif
-  x_stage_store(xs, xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, RSU, tid, blockDim.x, xpos);
+  x_stage_store(xs, xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, RSU, tid, NT, xpos);
   __syncthreads();
   W4A16_STAMP(t_barrier);
 #ifdef W4A16_TRACE
@@ -506,7 +516,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   const float ig0 = 1.0f / gv0;
   const float ig1 = FUSED ? 1.0f / gv1 : 1.0f;
   const int nrows = row_hi - row_lo;
-  for (int n = tid; n < nrows; n += blockDim.x) {
+  for (int n = tid; n < nrows; n += NT) {
     const int t = n / RT, rt = n - t * RT;
     const int w0 = tw0[t], w1 = tw1[t];
     float v[MT], u[MT];
@@ -567,7 +577,7 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   constexpr int RT = QS * R;             // output rows per task
   constexpr int NA = R * P * 4;          // accumulators per lane
   constexpr int V = NA * 4;              // values in a segment partial: [acc][j]
-  const int W = blockDim.x >> 6;
+  const int W = blockDim.x >> 6, NT = blockDim.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.K, S = a.S, CRS = a.CRS;  // CRS: chunks per row in this K-slice
@@ -577,10 +587,10 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
   const int row_hi = row_lo + a.rq + (rb < a.rr ? 1 : 0);
   const int ntasks = (row_hi - row_lo + RT - 1) / RT;
-  const StreamSplit split{ntasks * CPL, W, CPL};
+  const StreamSplit split{ntasks * CPL, W, a.rW};
   const int s_begin = split.begin(wv);
   const int T = split.begin(wv + 1) - s_begin;
-  const int ft = s_begin / CPL, jj0 = s_begin - ft * CPL;  // first task, its first step
+  const int ft = div_small(s_begin, CPL, a.rCPL), jj0 = s_begin - ft * CPL;  // first task, its first step
   const int beta = lane >> 2, j = lane & 3;
   const int jr = FUSED ? (j & 1) : j;    // row within the quad
   const bool is_up = FUSED && (j >= 2);
@@ -634,7 +644,7 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   // ring slot 0 first: the weight stream starts as early in the (cold)
   // instruction stream as possible, and the first step needs it anyway
   issue(0);
-  x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, tid, blockDim.x);
+  x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
 #pragma unroll
   for (int d = 1; d < D; ++d) issue(d);
 #else
@@ -648,9 +658,9 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
   if (lane == 0) wft[wv] = T > 0 ? ft : kNoTask;
 #ifdef W4A16_WEIGHTS_FIRST
-  x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, tid, blockDim.x);
+  x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
 #endif
-  x_stage_store(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, RSU, tid, blockDim.x, xpos);
+  x_stage_store(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, a.rUPR, RSU, tid, NT, xpos);
   __syncthreads();
   W4A16_STAMP(t_barrier);
 #ifdef W4A16_TRACE
@@ -766,7 +776,7 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   const int M = a.M;
   const int nrows = row_hi - row_lo;
   // item o = n * 4P + m (rows m >= M are skipped): a constant divisor
-  for (int o = tid; o < nrows * 4 * P; o += blockDim.x) {
+  for (int o = tid; o < nrows * 4 * P; o += NT) {
     const int n = o / (4 * P), m = o - n * (4 * P);
     if (m >= M) continue;
     const int t = n / RT, rt = n - t * RT;
