@@ -7,7 +7,9 @@ Default workload (one JSON line on stdout): the square projection, K = N =
 scales + 4 B g) per call / time per call, plus % of the 8 TB/s HBM peak.
 
 `--extra` also times the fused gate/up (M = 1, 7) and down (M = 1, 2, 4, 7,
-8) configurations and reports them under "extra" in the same line.
+8) configurations, and `--tower` the full-tower decode sweep (64 layers of
+gate/up + SwiGLU, down and q/k/v/o plus the 248320-wide head, one HIP graph
+replay per token, M = 1 and 7); both report under "extra" in the same line.
 
 The timed region brackets the calls with HIP events recorded on the stream
 the kernels run on; inputs are resident in HBM before timing starts.
@@ -237,6 +239,78 @@ def bench_extra(dev, stream, cycles=10):
     return out
 
 
+def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
+    """Full-tower decode sweep, one token = one HIP graph replay of
+    `layers` x (fused gate/up + SwiGLU 5120 -> 2 x 17408, down 17408 -> 5120,
+    q, k, v, o 5120 -> 5120) followed by the 5120 -> 248320 head GEMV: 385
+    launches and 14.1 GB of distinct weight allocations per token.  The MLP
+    chain is wired (SwiGLU output feeds down, down's output feeds the next
+    layer's gate/up); q/k/v/o and the head read fixed synthetic activations
+    (there is no attention).  Weights per layer are byte-identical replicas of
+    one encoded matrix per kind; the head matrix tiles the rows of the square
+    matrix (48.5 copies of its 5120 rows), since HBM traffic depends on the
+    addresses read, not on the values."""
+    import torch
+    import block_scaled_fp4_w4a16_amd as w4
+    import synth
+    H, F, V = 5120, 17408, 248320
+    cg, cd, cs = synth.CONFIGS["gate_up"], synth.CONFIGS["down"], synth.CONFIGS["square"]
+    log(f"[bench] tower: encoding gate/up/down/square, {layers} layers + head")
+    enc = {
+        "gate": synth.nvfp4_weights(cg["seed_gate"], F, H),
+        "up": synth.nvfp4_weights(cg["seed_up"], F, H),
+        "down": synth.nvfp4_weights(cd["seed_w"], H, F),
+        "sq": synth.nvfp4_weights(cs["seed_w"], H, H),
+    }
+    dev_enc = {k: (to_dev_u8(v[0], dev), to_dev_u8(v[1], dev),
+                   torch.tensor([v[2]], dtype=torch.float32, device=dev)) for k, v in enc.items()}
+
+    def copies(kind, n):
+        return [tuple(t.clone() for t in dev_enc[kind]) for _ in range(n)]
+    L = {"gate": copies("gate", layers), "up": copies("up", layers), "down": copies("down", layers),
+         "q": copies("sq", layers), "k": copies("sq", layers), "v": copies("sq", layers),
+         "o": copies("sq", layers)}
+    reps = (V + H - 1) // H
+    head = (torch.cat([dev_enc["sq"][0]] * reps)[:V].contiguous(),
+            torch.cat([dev_enc["sq"][1]] * reps)[:V].contiguous(), dev_enc["sq"][2].clone())
+    del dev_enc
+    b_layer = 2 * weight_bytes(F, H) + weight_bytes(H, F) + 4 * weight_bytes(H, H)
+    b_token = layers * b_layer + weight_bytes(V, H)
+    out = {}
+    for M in Ms:
+        x0 = to_dev_bf16(synth.activations(cg["seed_x"], M, H), dev)
+        xa = to_dev_bf16(synth.activations(cs["seed_x"], M, H), dev)
+        h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+        xs = [torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        ya = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+        wk_gu = w4.new_workspace(M, F, H, dev, fused=True)
+        wk_dn = w4.new_workspace(M, H, F, dev)
+        wk_sq = w4.new_workspace(M, H, H, dev)
+        wk_hd = w4.new_workspace(M, V, H, dev)
+
+        def token(s):
+            x = x0
+            for i in range(layers):
+                g, u, d = L["gate"][i], L["up"][i], L["down"][i]
+                w4.gemm_gate_up_swiglu(g[0], g[1], g[2], u[0], u[1], u[2], x, y=h, workspace=wk_gu, stream=s)
+                nx = xs[i % 2]
+                w4.gemm(d[0], d[1], d[2], h, y=nx, workspace=wk_dn, stream=s)
+                for kind in ("q", "k", "v", "o"):
+                    q = L[kind][i]
+                    w4.gemm(q[0], q[1], q[2], xa, y=ya, workspace=wk_sq, stream=s)
+                x = nx
+            w4.gemm(head[0], head[1], head[2], x, y=logits, workspace=wk_hd, stream=s)
+
+        t = graph_time([token], replays, stream)
+        out[f"tower_M{M}"] = dict(ms_per_token=t * 1e3, tokens_per_s=1.0 / t, launches_per_token=6 * layers + 1,
+                                  bytes_per_token=b_token, gbs=b_token / t / 1e9,
+                                  pct_peak=100 * b_token / t / 1e9 / HBM_PEAK_GBS)
+        log(f"[bench] tower M={M}: {t*1e3:.3f} ms/token ({1/t:.1f} tok/s), {b_token/t/1e9:.0f} GB/s "
+            f"over {b_token/1e9:.2f} GB")
+    return out
+
+
 def cpu_baseline(seconds_target=12.0):
     """The CPU oracle timed on a bounded sample of the square workload."""
     import oracle
@@ -312,6 +386,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--extra", action="store_true", help="also time the gate/up and down configs")
+    ap.add_argument("--tower", action="store_true",
+                    help="also time the full-tower decode sweep (64 layers + head, 14.1 GB, M = 1 and 7)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", choices=["bench", "copy", "ingest-pmc"], default="bench",
                     help="copy: run only the PMC calibration copy kernel; ingest-pmc: turn rocprofv3 "
@@ -339,6 +415,8 @@ def main():
     log(f"[bench] square (graph replay): {r['per_call']*1e6:.3f} us/call, {r['gbs']:.1f} GB/s; "
         f"eager: {r['eager_per_call']*1e6:.3f} us/call, {r['eager_gbs']:.1f} GB/s")
     extra = bench_extra(dev, stream) if args.extra else None
+    if args.tower:
+        extra = dict(extra or {}, **bench_tower(dev, stream))
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": "effective weight GB/s (NVFP4 codes + E4M3 scales + g per call / time per call), W4A16 GEMV",
