@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["gemm", "gemm_gate_up_swiglu", "dequant", "workspace_size",
+__all__ = ["gemm", "gemm_gate_up_swiglu", "dequant", "quantize", "workspace_size",
            "workspace_size_gate_up", "new_workspace", "W4A16Error", "library_path", "lib", "MAX_M"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +56,12 @@ def lib():
     L.w4a16_gemm_gate_up_swiglu.restype = I
     L.w4a16_dequant.argtypes = [P, P, P, P, I, I, P]
     L.w4a16_dequant.restype = I
+    L.w4a16_quantize.argtypes = [P, P, P, P, I, I, P, Z, P]
+    L.w4a16_quantize.restype = I
+    L.w4a16_quantize_bf16.argtypes = [P, P, P, P, I, I, P, Z, P]
+    L.w4a16_quantize_bf16.restype = I
+    L.w4a16_quantize_workspace_size.argtypes = [I, I]
+    L.w4a16_quantize_workspace_size.restype = Z
     L.w4a16_workspace_size.argtypes = [I, I, I]
     L.w4a16_workspace_size.restype = Z
     L.w4a16_workspace_size_gate_up.argtypes = [I, I, I]
@@ -181,6 +187,34 @@ def gemm_gate_up_swiglu(wq_gate, ws_gate, g_gate, wq_up, ws_up, g_up, x, y=None,
     if st != OK:
         raise W4A16Error(st, "w4a16_gemm_gate_up_swiglu")
     return y
+
+
+def quantize(w, wq=None, ws=None, g=None, workspace=None, stream=None):
+    """NVFP4-encode w[N, K] (float32 or bfloat16): returns (wq u8 [N, K/2],
+    ws u8 [N, K/16], g float32 [1]), bit-exact to the fp64 recipe."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"w must be float32 or bfloat16, got {w.dtype}")
+    _check(w, "w", w.dtype, 2)
+    N, K = w.shape
+    dev = w.device
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=dev) if wq is None else wq
+    ws = torch.empty((N, K // 16), dtype=torch.uint8, device=dev) if ws is None else ws
+    g = torch.empty((1,), dtype=torch.float32, device=dev) if g is None else g
+    _check(wq, "wq", torch.uint8, 2)
+    _check(ws, "ws", torch.uint8, 2)
+    _check(g, "g", torch.float32, None)
+    if tuple(wq.shape) != (N, K // 2) or tuple(ws.shape) != (N, K // 16) or g.numel() != 1:
+        raise ValueError("wq, ws, g do not match w's shape")
+    need = int(lib().w4a16_quantize_workspace_size(N, K))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", workspace.dtype, None)
+    fn = lib().w4a16_quantize if w.dtype == torch.float32 else lib().w4a16_quantize_bf16
+    st = fn(_ptr(w), _ptr(wq), _ptr(ws), _ptr(g), N, K, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != OK:
+        raise W4A16Error(st, "w4a16_quantize")
+    return wq, ws, g
 
 
 def dequant(wq, ws, g, w=None, stream=None):

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "w4a16_kernels.h"
+#include "w4a16_quant.h"
 
 namespace w4a16 {
 namespace {
@@ -378,6 +379,63 @@ w4a16_status_t w4a16_dequant(const uint8_t* wq, const uint8_t* ws, const float* 
   hipLaunchKernelGGL(k_dequant, dim3((unsigned)blocks), dim3(256), 0, stream, wq, ws, g, w, words,
                      K);
   return hipGetLastError() == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace w4a16 {
+namespace {
+
+// Pass-1 workgroups of the quantiser (its workspace holds one float each).
+int quant_parts(long long count) {
+  long long p = (count + 255) / 256;
+  const long long cap = 4LL * cu_count();
+  if (p > cap) p = cap;
+  return (int)(p > 0 ? p : 1);
+}
+
+template <typename T>
+w4a16_status_t run_quantize(const T* w, uint8_t* wq, uint8_t* ws, float* g, int N, int K,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!w || !wq || !ws || !g || !workspace) return W4A16_ERR_INVALID_VALUE;
+  if (N <= 0 || K <= 0) return W4A16_ERR_INVALID_VALUE;
+  if (K % 16 != 0) return W4A16_ERR_UNSUPPORTED;
+  if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(g, 4) || !aligned(workspace, 16))
+    return W4A16_ERR_UNSUPPORTED;
+  const long long count = (long long)N * K;
+  const int parts = quant_parts(count);
+  if (workspace_bytes < (size_t)parts * sizeof(float)) return W4A16_ERR_INVALID_VALUE;
+  float* part = static_cast<float*>(workspace);
+  hipLaunchKernelGGL(k_quant_amax<T>, dim3((unsigned)parts), dim3(256), 0, stream, w, count, part);
+  if (hipGetLastError() != hipSuccess) return W4A16_ERR_LAUNCH;
+  const long long nblocks = count / 16;
+  long long grid = (nblocks + 255) / 256;
+  const long long cap = 8LL * cu_count();
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(k_quant_encode<T>, dim3((unsigned)grid), dim3(256), 0, stream, w, nblocks,
+                     part, parts, wq, ws, g);
+  return hipGetLastError() == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace w4a16
+
+extern "C" {
+
+size_t w4a16_quantize_workspace_size(int N, int K) {
+  if (N <= 0 || K <= 0 || K % 16 != 0) return 0;
+  return ((size_t)quant_parts((long long)N * K) * sizeof(float) + 255) / 256 * 256;
+}
+
+w4a16_status_t w4a16_quantize(const float* w, uint8_t* wq, uint8_t* ws, float* g, int N, int K,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_quantize(w, wq, ws, g, N, K, workspace, workspace_bytes, stream);
+}
+
+w4a16_status_t w4a16_quantize_bf16(const uint16_t* w, uint8_t* wq, uint8_t* ws, float* g, int N,
+                                   int K, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return run_quantize(w, wq, ws, g, N, K, workspace, workspace_bytes, stream);
 }
 
 const char* w4a16_status_string(w4a16_status_t status) {

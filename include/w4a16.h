@@ -110,6 +110,36 @@ w4a16_status_t w4a16_gemm_gate_up_swiglu(const uint8_t* wq_gate, const uint8_t* 
 w4a16_status_t w4a16_dequant(const uint8_t* wq, const uint8_t* ws, const float* g, float* w,
                              int N, int K, hipStream_t stream);
 
+/*
+ * NVFP4 encoding of a weight matrix w[N][K] (fp32: w4a16_quantize; bf16 bit
+ * patterns: w4a16_quantize_bf16) into the schema above.  The pages give the
+ * schema, not the block-scale recipe; the recipe implemented is:
+ *   amax = max |w|;  g = fp32(448 / amax)  (g = 1 when amax = 0);
+ *   per 16-input block: S = the E4M3FN value nearest to max|w_block| * g / 6
+ *   (ties to the even code, saturating at 448); if S = 0 the block's codes
+ *   are 0, else each code is the E2M1 value nearest to w * g / S (ties to the
+ *   even code, saturating at 6, sign kept, so -0 can occur);
+ *   all in fp64 in that order.  Every output byte and g equal the scalar fp64
+ *   evaluation of that recipe (bit-exact).
+ *   w, wq : 16-byte aligned;  g : one fp32 in device memory, 4-byte aligned;
+ *   K % 16 == 0 (the matmul entry points further need K % 256 == 0).
+ *   workspace : at least w4a16_quantize_workspace_size(N, K) bytes, 16-byte
+ *               aligned, no initialisation needed.
+ *   Inputs are expected finite: NaN elements are ignored by the maxima, and an
+ *   infinite element makes g = 0 and every code 0.
+ * For converting a higher-precision checkpoint at load time (FlashRT §0/§1
+ * convert checkpoints to NVFP4 before serving; qwentin packs 4-bit weights on
+ * the GPU at conversion).
+ */
+w4a16_status_t w4a16_quantize(const float* w, uint8_t* wq, uint8_t* ws, float* g, int N, int K,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+w4a16_status_t w4a16_quantize_bf16(const uint16_t* w, uint8_t* wq, uint8_t* ws, float* g, int N,
+                                   int K, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/* Bytes of workspace w4a16_quantize[_bf16] needs (0 = unsupported shape). */
+size_t w4a16_quantize_workspace_size(int N, int K);
+
 /* Bytes of workspace w4a16_gemm needs for this shape (0 = none, or an
  * unsupported shape). */
 size_t w4a16_workspace_size(int M, int N, int K);

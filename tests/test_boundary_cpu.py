@@ -122,3 +122,28 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros((1, 256), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         w4.gemm(wq, ws, g, x)
+
+
+def call_quant(lib, w=P, wq=P, ws=P, g=P, N=4, K=32, work=P, wbytes=4096, bf16=False):
+    fn = lib.w4a16_quantize_bf16 if bf16 else lib.w4a16_quantize
+    return fn(w, wq, ws, g, N, K, work, wbytes, None)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_quantize_argument_checks(lib, bf16):
+    for arg in ("w", "wq", "ws", "g", "work"):
+        assert call_quant(lib, bf16=bf16, **{arg: 0}) == w4.ERR_INVALID_VALUE, arg
+    assert call_quant(lib, bf16=bf16, N=0) == w4.ERR_INVALID_VALUE
+    assert call_quant(lib, bf16=bf16, K=-16) == w4.ERR_INVALID_VALUE
+    assert call_quant(lib, bf16=bf16, K=24) == w4.ERR_UNSUPPORTED          # K % 16 != 0
+    assert call_quant(lib, bf16=bf16, w=P + 8) == w4.ERR_UNSUPPORTED
+    assert call_quant(lib, bf16=bf16, wq=P + 8) == w4.ERR_UNSUPPORTED
+    assert call_quant(lib, bf16=bf16, g=P + 2) == w4.ERR_UNSUPPORTED
+    assert call_quant(lib, bf16=bf16, wbytes=0) == w4.ERR_INVALID_VALUE   # short workspace
+
+
+def test_quantize_workspace_size(lib):
+    assert lib.w4a16_quantize_workspace_size(5120, 5120) >= 4
+    assert lib.w4a16_quantize_workspace_size(5120, 5120) % 256 == 0
+    assert lib.w4a16_quantize_workspace_size(3, 24) == 0
+    assert lib.w4a16_quantize_workspace_size(0, 32) == 0
