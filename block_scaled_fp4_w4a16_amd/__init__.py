@@ -19,7 +19,8 @@ import os
 
 import torch
 
-__all__ = ["gemm", "gemm_gate_up_swiglu", "dequant", "quantize", "workspace_size",
+__all__ = ["gemm", "gemm_gate_up_swiglu", "gemm_argmax", "dequant", "quantize", "workspace_size",
+           "workspace_size_argmax",
            "workspace_size_gate_up", "new_workspace", "W4A16Error", "library_path", "lib", "MAX_M"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,6 +57,10 @@ def lib():
     L.w4a16_gemm_gate_up_swiglu.restype = I
     L.w4a16_dequant.argtypes = [P, P, P, P, I, I, P]
     L.w4a16_dequant.restype = I
+    L.w4a16_gemm_argmax.argtypes = [P, P, P, P, P, P, I, I, I, P, Z, P]
+    L.w4a16_gemm_argmax.restype = I
+    L.w4a16_workspace_size_argmax.argtypes = [I, I, I]
+    L.w4a16_workspace_size_argmax.restype = Z
     L.w4a16_quantize.argtypes = [P, P, P, P, I, I, P, Z, P]
     L.w4a16_quantize.restype = I
     L.w4a16_quantize_bf16.argtypes = [P, P, P, P, I, I, P, Z, P]
@@ -187,6 +192,37 @@ def gemm_gate_up_swiglu(wq_gate, ws_gate, g_gate, wq_up, ws_up, g_up, x, y=None,
     if st != OK:
         raise W4A16Error(st, "w4a16_gemm_gate_up_swiglu")
     return y
+
+
+def workspace_size_argmax(M: int, N: int, K: int) -> int:
+    return int(lib().w4a16_workspace_size_argmax(M, N, K))
+
+
+def gemm_argmax(wq, ws, g, x, idx=None, val=None, workspace=None, stream=None):
+    """Greedy selection over the head: (idx int32 [M], val float32 [M]) with
+    idx[m] = argmax_n fp32(x[m] . W[n] / g) (ties to the smaller n) and val[m]
+    that logit; no logits are materialised."""
+    N, K = _weights(wq, ws, g, "")
+    _check(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError(f"x has K={x.shape[1]}, weights have K={K}")
+    idx = torch.empty((M,), dtype=torch.int32, device=x.device) if idx is None else idx
+    val = torch.empty((M,), dtype=torch.float32, device=x.device) if val is None else val
+    _check(idx, "idx", torch.int32, 1)
+    _check(val, "val", torch.float32, 1)
+    if idx.numel() != M or val.numel() != M:
+        raise ValueError(f"idx and val must have {M} elements")
+    need = workspace_size_argmax(M, N, K) if M <= MAX_M else 0
+    if workspace is None:
+        workspace = torch.zeros(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(workspace, "workspace", workspace.dtype, None)
+    st = lib().w4a16_gemm_argmax(_ptr(wq), _ptr(ws), _ptr(g), _ptr(x), _ptr(idx), _ptr(val), M, N, K,
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    if st != OK:
+        raise W4A16Error(st, "w4a16_gemm_argmax")
+    return idx, val
 
 
 def quantize(w, wq=None, ws=None, g=None, workspace=None, stream=None):

@@ -63,7 +63,7 @@ struct KernEntry {
   bool mfma;
   int rows;   // VALU: MT (= M); MFMA: P (activation-row passes of 4)
   int lr, D;
-  bool fused;
+  int epi;    // epilogue: kEpiPlain, kEpiSwiglu or kEpiArgmax
   int LB;
   const void* fn;
 };
@@ -89,19 +89,24 @@ struct KernEntry {
   W4A16_MFMA_ALL_P(1, 8, F, 512) W4A16_MFMA_ALL_P(1, 16, F, 512)                   \
   W4A16_MFMA_ALL_P(2, 4, F, 512) W4A16_MFMA_ALL_P(2, 8, F, 512)                    \
   W4A16_MFMA_ALL_P(2, 8, F, 1024) W4A16_MFMA_ALL_P(4, 4, F, 512)
-#else
-#define W4A16_VALU_SET(F)                                                          \
+#endif
+// the launch rules' variants (the argmax epilogue exists only in these)
+#define W4A16_VALU_BASE(F)                                                         \
   W4A16_VALU_ALL_MT(8, 4, F, 1024) W4A16_VALU_ALL_MT(16, 4, F, 1024)               \
   W4A16_VALU_ALL_MT(32, 4, F, 1024)
-#define W4A16_MFMA_SET(F) W4A16_MFMA_ALL_P(2, 4, F, 512)
+#define W4A16_MFMA_BASE(F) W4A16_MFMA_ALL_P(2, 4, F, 512)
+#ifndef W4A16_TUNING
+#define W4A16_VALU_SET(F) W4A16_VALU_BASE(F)
+#define W4A16_MFMA_SET(F) W4A16_MFMA_BASE(F)
 #endif
 
 const KernEntry kKernels[] = {
-    W4A16_VALU_SET(false) W4A16_VALU_SET(true) W4A16_MFMA_SET(false) W4A16_MFMA_SET(true)};
+    W4A16_VALU_SET(kEpiPlain) W4A16_VALU_SET(kEpiSwiglu) W4A16_VALU_BASE(kEpiArgmax)
+    W4A16_MFMA_SET(kEpiPlain) W4A16_MFMA_SET(kEpiSwiglu) W4A16_MFMA_BASE(kEpiArgmax)};
 
-const KernEntry* find_kernel(bool mfma, int rows, int lr, int D, bool fused, int LB) {
+const KernEntry* find_kernel(bool mfma, int rows, int lr, int D, int epi, int LB) {
   for (const KernEntry& e : kKernels)
-    if (e.mfma == mfma && e.rows == rows && e.lr == lr && e.D == D && e.fused == fused &&
+    if (e.mfma == mfma && e.rows == rows && e.lr == lr && e.D == D && e.epi == epi &&
         e.LB == LB)
       return &e;
   return nullptr;
@@ -133,9 +138,10 @@ struct Override {
 Override g_override{};
 #endif
 
-// Kernel selection is a pure function of (M, N, K, fused) and the device's
+// Kernel selection is a pure function of (M, N, K, epilogue) and the device's
 // compute-unit count.
-Plan plan_gemm(int M, int N, int K, bool fused) {
+Plan plan_gemm(int M, int N, int K, int epi) {
+  const bool fused = epi == kEpiSwiglu;
   Plan pl{};
   const int cus = cu_count();
   const int CR = K >> 5;  // 16-byte chunks per weight row (a multiple of 8)
@@ -174,7 +180,7 @@ Plan plan_gemm(int M, int N, int K, bool fused) {
   if (wmax > pl.LB / 64) wmax = pl.LB / 64;
   // keep wg_per_cu workgroups resident together
   const KernEntry* ke =
-      find_kernel(pl.mfma, pl.mfma ? (M + 3) / 4 : M, pl.lr, pl.D, fused, pl.LB);
+      find_kernel(pl.mfma, pl.mfma ? (M + 3) / 4 : M, pl.lr, pl.D, epi, pl.LB);
   if (!ke) return Plan{};
   const int wocc = waves_per_cu(ke) / wg_per_cu;
   int wcap = wmax < wocc ? wmax : wocc;
@@ -237,9 +243,16 @@ Plan plan_gemm(int M, int N, int K, bool fused) {
     pl.W = W;
     pl.kmax = (int)kmax;
     pl.lds = lds;
-    pl.ws = S > 1 ? kCounterBytes +
-                        (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1)
-                  : 0;
+    if (epi == kEpiArgmax) {
+      // argmax: no K split; the arrival counter, then one (value, index)
+      // candidate per workgroup and activation row
+      if (S > 1) return Plan{};
+      pl.ws = kCounterBytes + (size_t)pl.nrb * (size_t)M * 2 * sizeof(float);
+    } else {
+      pl.ws = S > 1 ? kCounterBytes +
+                          (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1)
+                    : 0;
+    }
     return pl;
   }
   return Plan{};  // no split fits (pl.S == 0): unsupported
@@ -257,9 +270,9 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t dispatch(const Plan& pl, bool fused, hipStream_t s, const MatArgs& a) {
+hipError_t dispatch(const Plan& pl, int epi, hipStream_t s, const MatArgs& a) {
   const int rows = pl.mfma ? (a.M + 3) / 4 : a.M;
-  const KernEntry* k = find_kernel(pl.mfma, rows, pl.lr, pl.D, fused, pl.LB);
+  const KernEntry* k = find_kernel(pl.mfma, rows, pl.lr, pl.D, epi, pl.LB);
   if (!k || pl.W * 64 > pl.LB) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)pl.nrb, (unsigned)pl.S), block((unsigned)(pl.W * 64));
   return launch(k->fn, grid, block, pl.lds, s, a);
@@ -272,14 +285,14 @@ w4a16_status_t check_shape(int M, int N, int K) {
   return W4A16_OK;
 }
 
-size_t workspace_bytes_for(int M, int N, int K, bool fused) {
+size_t workspace_bytes_for(int M, int N, int K, int epi) {
   if (check_shape(M, N, K) != W4A16_OK) return 0;
-  return plan_gemm(M, N, K, fused).ws;
+  return plan_gemm(M, N, K, epi).ws;
 }
 
-w4a16_status_t run_matmul(MatArgs a, bool fused, void* workspace, size_t workspace_bytes,
+w4a16_status_t run_matmul(MatArgs a, int epi, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-  const Plan pl = plan_gemm(a.M, a.N, a.K, fused);
+  const Plan pl = plan_gemm(a.M, a.N, a.K, epi);
   if (pl.S == 0 || pl.lds > kMaxLds) return W4A16_ERR_UNSUPPORTED;
   if (workspace_bytes < pl.ws || (pl.ws > 0 && workspace == nullptr))
     return W4A16_ERR_INVALID_VALUE;
@@ -295,7 +308,8 @@ w4a16_status_t run_matmul(MatArgs a, bool fused, void* workspace, size_t workspa
   a.rUPR = 1.0f / (float)(a.CRS * 4);
   a.cnt = static_cast<int*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-  const hipError_t e = dispatch(pl, fused, stream, a);
+  a.cand = a.part;
+  const hipError_t e = dispatch(pl, epi, stream, a);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
@@ -306,10 +320,14 @@ using namespace w4a16;
 
 extern "C" {
 
-size_t w4a16_workspace_size(int M, int N, int K) { return workspace_bytes_for(M, N, K, false); }
+size_t w4a16_workspace_size(int M, int N, int K) { return workspace_bytes_for(M, N, K, kEpiPlain); }
 
 size_t w4a16_workspace_size_gate_up(int M, int N, int K) {
-  return workspace_bytes_for(M, N, K, true);
+  return workspace_bytes_for(M, N, K, kEpiSwiglu);
+}
+
+size_t w4a16_workspace_size_argmax(int M, int N, int K) {
+  return workspace_bytes_for(M, N, K, kEpiArgmax);
 }
 
 w4a16_status_t w4a16_gemm(const uint8_t* wq, const uint8_t* ws, const float* g,
@@ -333,7 +351,7 @@ w4a16_status_t w4a16_gemm(const uint8_t* wq, const uint8_t* ws, const float* g,
   a.M = M;
   a.N = N;
   a.K = K;
-  return run_matmul(a, false, workspace, workspace_bytes, stream);
+  return run_matmul(a, kEpiPlain, workspace, workspace_bytes, stream);
 }
 
 w4a16_status_t w4a16_gemm_gate_up_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,
@@ -362,7 +380,33 @@ w4a16_status_t w4a16_gemm_gate_up_swiglu(const uint8_t* wq_gate, const uint8_t* 
   a.M = M;
   a.N = N;
   a.K = K;
-  return run_matmul(a, true, workspace, workspace_bytes, stream);
+  return run_matmul(a, kEpiSwiglu, workspace, workspace_bytes, stream);
+}
+
+w4a16_status_t w4a16_gemm_argmax(const uint8_t* wq, const uint8_t* ws, const float* g,
+                                 const uint16_t* x, int32_t* idx, float* val, int M, int N, int K,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!wq || !ws || !g || !x || !idx || !val) return W4A16_ERR_INVALID_VALUE;
+  w4a16_status_t st = check_shape(M, N, K);
+  if (st != W4A16_OK) return st;
+  if (!aligned(wq, 16) || !aligned(ws, 16) || !aligned(x, 16) || !aligned(g, 4) ||
+      !aligned(idx, 4) || !aligned(val, 4))
+    return W4A16_ERR_UNSUPPORTED;
+  MatArgs a{};
+  a.wq0 = wq;
+  a.ws0 = ws;
+  a.g0 = g;
+  a.wq1 = wq;
+  a.ws1 = ws;
+  a.g1 = g;
+  a.x = x;
+  a.y = nullptr;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.amax_idx = idx;
+  a.amax_val = val;
+  return run_matmul(a, kEpiArgmax, workspace, workspace_bytes, stream);
 }
 
 w4a16_status_t w4a16_dequant(const uint8_t* wq, const uint8_t* ws, const float* g, float* w,
@@ -464,9 +508,9 @@ __attribute__((visibility("default"))) int w4a16_tuning_set(int enable, int mfma
 }
 // Tuning builds only: the launch plan for a shape, as 12 ints
 // {mfma, lr, D, W, LB, nrb, S, rq, rr, kmax, lds, ws (bytes, clamped)}.
-__attribute__((visibility("default"))) void w4a16_tuning_plan(int M, int N, int K, int fused,
+__attribute__((visibility("default"))) void w4a16_tuning_plan(int M, int N, int K, int epi,
                                                                long long* out) {
-  const Plan pl = plan_gemm(M, N, K, fused != 0);
+  const Plan pl = plan_gemm(M, N, K, epi);
   const long long v[12] = {pl.mfma, pl.lr, pl.D, pl.W, pl.LB, pl.nrb, pl.S,
                            pl.rq, pl.rr, pl.kmax, (long long)pl.lds, (long long)pl.ws};
   for (int i = 0; i < 12; ++i) out[i] = v[i];

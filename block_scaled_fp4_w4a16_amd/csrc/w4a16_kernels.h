@@ -57,7 +57,17 @@ struct MatArgs {
   // fp32 reciprocals of the launch's divisors (waves per workgroup, chunk
   // steps per task, x units per row), for div_small
   float rW, rCPL, rUPR;
+  // argmax epilogue: per-workgroup candidates (value, index bits) [nwg][M],
+  // and the results idx[M], val[M]
+  float* cand;
+  int* amax_idx;
+  float* amax_val;
 };
+
+// Epilogue of the matmul kernels: y = bf16(x W^T / g); y = bf16(silu(gate)
+// * up) from two matrices; or, instead of y, the row index of the largest
+// fp32 logit x W^T / g for each activation row (greedy decoding of a head).
+constexpr int kEpiPlain = 0, kEpiSwiglu = 1, kEpiArgmax = 2;
 
 #define W4A16_DEV __device__ __forceinline__
 
@@ -289,6 +299,70 @@ W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, fl
 }
 
 // ---------------------------------------------------------------------------
+// Argmax epilogue.  Order: larger value first, then the smaller row index, so
+// the result does not depend on the order in which candidates meet; a NaN
+// logit never wins (comparisons with NaN are false); if every logit of a row
+// is NaN the index is -1.  Each workgroup reduces its rows to one candidate
+// per activation row m and stores it with agent-scope stores; the last
+// workgroup to finish (arrival counter cnt[0], zeroed again by that
+// workgroup) reduces the candidates of all workgroups.
+// ---------------------------------------------------------------------------
+W4A16_DEV void argmax_take(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+// Workgroup-wide argmax of one (v, i) per thread; the result is valid in
+// thread 0.  red: LDS scratch of at least 2 words per wave.
+W4A16_DEV void wg_argmax(float& v, int& i, float* red, int W) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(v, off);
+    const int oi = __shfl_xor(i, off);
+    argmax_take(v, i, ov, oi);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    red[2 * w] = v;
+    red[2 * w + 1] = __int_as_float(i);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int k = 1; k < W; ++k) argmax_take(v, i, red[2 * k], __float_as_int(red[2 * k + 1]));
+  __syncthreads();
+}
+constexpr int kNoIndex = 0x7fffffff;
+
+// Called by every thread once the workgroup's candidates cand[rb][m] are
+// stored: the last workgroup reduces all of them into idx[m], val[m].
+W4A16_DEV void argmax_finish(const MatArgs& a, int nwg, float* red, int W) {
+  __shared__ int is_last;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int before = __hip_atomic_fetch_add(a.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = before == nwg - 1;
+    if (is_last) __hip_atomic_store(a.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  for (int m = 0; m < a.M; ++m) {
+    float bv = -__builtin_inff();
+    int bi = kNoIndex;
+    for (int b = threadIdx.x; b < nwg; b += W * 64) {
+      const float* c = a.cand + ((size_t)b * a.M + m) * 2;
+      argmax_take(bv, bi, load_coherent(c), __float_as_int(load_coherent(c + 1)));
+    }
+    wg_argmax(bv, bi, red, W);
+    if (threadIdx.x == 0) {
+      a.amax_idx[m] = bi == kNoIndex ? -1 : bi;
+      a.amax_val[m] = bv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Work split inside a workgroup (both matmul kernels).  The workgroup's rows
 // form ntasks tasks (row groups); a task is CPL chunk steps along K, so the
 // workgroup has TS = ntasks * CPL steps, step s = task * CPL + jj.  Wave w
@@ -323,8 +397,9 @@ constexpr int kNoTask = 1 << 30;
 // (swizzled) and are read with 128-bit LDS loads; lanes of different slots
 // read the same x (broadcast).
 // ---------------------------------------------------------------------------
-template <int MT, int L, int D, bool FUSED, int LB>
+template <int MT, int L, int D, int EPI, int LB>
 __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
+  constexpr bool FUSED = EPI == kEpiSwiglu;
   W4A16_STAMP(t_start);
   extern __shared__ uint4 xs[];
   constexpr int G = 64 / L;
@@ -516,6 +591,32 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   const float ig0 = 1.0f / gv0;
   const float ig1 = FUSED ? 1.0f / gv1 : 1.0f;
   const int nrows = row_hi - row_lo;
+  if (EPI == kEpiArgmax) {
+    // S == 1 here (the host rejects a K split with this epilogue); x is no
+    // longer needed, so its LDS holds the reduction scratch
+    float* red = reinterpret_cast<float*>(xs);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float bv = -__builtin_inff();
+      int bi = kNoIndex;
+      for (int n = tid; n < nrows; n += NT) {
+        const int t = n / RT, rt = n - t * RT;
+        float v = 0.0f;
+        for (int w = tw0[t]; w <= tw1[t]; ++w) {
+          const int k = t - wft[w];
+          if (k >= 0) v += seg[(w * a.kmax + k) * V + rt * MT + m];
+        }
+        argmax_take(bv, bi, v * ig0, row_lo + n);
+      }
+      wg_argmax(bv, bi, red, W);
+      if (tid == 0) {
+        float* c = a.cand + ((size_t)rb * a.M + m) * 2;
+        store_coherent(c, bv);
+        store_coherent(c + 1, __int_as_float(bi));
+      }
+    }
+    argmax_finish(a, gridDim.x, red, W);
+  } else
   for (int n = tid; n < nrows; n += NT) {
     const int t = n / RT, rt = n - t * RT;
     const int w0 = tw0[t], w1 = tw1[t];
@@ -569,8 +670,9 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 // 16 B = 256 contiguous bytes per row per load) and the x slice of activation
 // row 4*pp + j from LDS, which then feeds the MFMAs of all R quads.
 // ---------------------------------------------------------------------------
-template <int P, int R, int D, bool FUSED, int LB>
+template <int P, int R, int D, int EPI, int LB>
 __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
+  constexpr bool FUSED = EPI == kEpiSwiglu;
   W4A16_STAMP(t_start);
   extern __shared__ uint4 xs[];
   constexpr int QS = FUSED ? 2 : 4;      // output rows per quad
@@ -775,6 +877,33 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   const float ig1 = FUSED ? 1.0f / gv1 : 1.0f;
   const int M = a.M;
   const int nrows = row_hi - row_lo;
+  if (EPI == kEpiArgmax) {
+    // S == 1 here (the host rejects a K split with this epilogue); x is no
+    // longer needed, so its LDS holds the reduction scratch
+    float* red = reinterpret_cast<float*>(xs);
+    for (int m = 0; m < M; ++m) {
+      float bv = -__builtin_inff();
+      int bi = kNoIndex;
+      for (int n = tid; n < nrows; n += NT) {
+        const int t = n / RT, rt = n - t * RT;
+        const int rr = rt / QS, jo = rt - rr * QS;
+        const int idx = (rr * (4 * P) + m) * 4 + jo;
+        float v = 0.0f;
+        for (int w = tw0[t]; w <= tw1[t]; ++w) {
+          const int k = t - wft[w];
+          if (k >= 0) v += seg[(w * a.kmax + k) * V + idx];
+        }
+        argmax_take(bv, bi, v * ig0, row_lo + n);
+      }
+      wg_argmax(bv, bi, red, W);
+      if (tid == 0) {
+        float* c = a.cand + ((size_t)rb * M + m) * 2;
+        store_coherent(c, bv);
+        store_coherent(c + 1, __int_as_float(bi));
+      }
+    }
+    argmax_finish(a, gridDim.x, red, W);
+  } else
   // item o = n * 4P + m (rows m >= M are skipped): a constant divisor
   for (int o = tid; o < nrows * 4 * P; o += NT) {
     const int n = o / (4 * P), m = o - n * (4 * P);

@@ -102,6 +102,30 @@ w4a16_status_t w4a16_gemm_gate_up_swiglu(const uint8_t* wq_gate, const uint8_t* 
                                          hipStream_t stream);
 
 /*
+ * Head projection with greedy selection: for each activation row m, the row
+ * index n of the largest fp32 logit x[m] . W[n] / g (the value that the matmul
+ * would round to bf16), ties to the smaller n; a NaN logit is never selected
+ * (idx = -1 if every logit of a row is NaN).  idx[m] gets the index and
+ * val[m] that logit.  No logits are written.  The qwen36-fp4 README lists
+ * greedy sampling among its kernels and an option fusing the lm_head with a
+ * greedy argmax that avoids the logits buffer (its "CUDA Runtime Knobs").
+ *   idx : int32 [M], val : fp32 [M], both device memory, 4-byte aligned.
+ *   Other pointers, alignment and shape rules as w4a16_gemm, except that the
+ *   shape must not need a K split (the x rows a workgroup stages, M * K bf16
+ *   rounded up to whole passes, must fit in LDS), else W4A16_ERR_UNSUPPORTED.
+ *   workspace : at least w4a16_workspace_size_argmax(M, N, K) bytes (never 0
+ *               for a supported shape), 16-byte aligned; its first 4096 bytes
+ *               must be zero before the first call and are left zero by
+ *               every call; the rest needs no initialisation.
+ */
+w4a16_status_t w4a16_gemm_argmax(const uint8_t* wq, const uint8_t* ws, const float* g,
+                                 const uint16_t* x, int32_t* idx, float* val, int M, int N, int K,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace w4a16_gemm_argmax needs (0 = unsupported shape). */
+size_t w4a16_workspace_size_argmax(int M, int N, int K);
+
+/*
  * Dequantise to fp32: w[N][K] = e2m1 * e4m3 / g, the product exact and the
  * division IEEE fp32 (correctly rounded), so the result is bit-exact for
  * every finite value; a NaN scale gives NaN.  wq, ws : 16-byte aligned;

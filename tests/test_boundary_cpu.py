@@ -147,3 +147,15 @@ def test_quantize_workspace_size(lib):
     assert lib.w4a16_quantize_workspace_size(5120, 5120) % 256 == 0
     assert lib.w4a16_quantize_workspace_size(3, 24) == 0
     assert lib.w4a16_quantize_workspace_size(0, 32) == 0
+
+
+def test_argmax_argument_checks(lib):
+    def call(wq=P, ws=P, g=P, x=P, idx=P, val=P, M=1, N=64, K=256, work=P, wbytes=1 << 20):
+        return lib.w4a16_gemm_argmax(wq, ws, g, x, idx, val, M, N, K, work, wbytes, None)
+    for arg in ("wq", "ws", "g", "x", "idx", "val"):
+        assert call(**{arg: 0}) == w4.ERR_INVALID_VALUE, arg
+    assert call(work=0, wbytes=0) == w4.ERR_INVALID_VALUE     # the workspace is always required
+    assert call(idx=P + 2) == w4.ERR_UNSUPPORTED
+    assert call(M=17) == w4.ERR_UNSUPPORTED
+    assert w4.workspace_size_argmax(1, 248320, 5120) >= 4096 + 8
+    assert w4.workspace_size_argmax(16, 64, 17408) == 0        # would need a K split
