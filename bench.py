@@ -242,7 +242,8 @@ def bench_extra(dev, stream, cycles=10):
 def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
     """Full-tower decode sweep, one token = one HIP graph replay of
     `layers` x (fused gate/up + SwiGLU 5120 -> 2 x 17408, down 17408 -> 5120,
-    q, k, v, o 5120 -> 5120) followed by the 5120 -> 248320 head GEMV: 385
+    q, k, v, o 5120 -> 5120) followed by the 5120 -> 248320 head GEMV with
+    fused greedy argmax (the head alone is also timed with and without it): 385
     launches and 14.1 GB of distinct weight allocations per token.  The MLP
     chain is wired (SwiGLU output feeds down, down's output feeds the next
     layer's gate/up); q/k/v/o and the head read fixed synthetic activations
@@ -287,7 +288,10 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
         wk_gu = w4.new_workspace(M, F, H, dev, fused=True)
         wk_dn = w4.new_workspace(M, H, F, dev)
         wk_sq = w4.new_workspace(M, H, H, dev)
-        wk_hd = w4.new_workspace(M, V, H, dev)
+        wk_hd0 = w4.new_workspace(M, V, H, dev)
+        wk_hd = torch.zeros(w4.workspace_size_argmax(M, V, H), dtype=torch.uint8, device=dev)
+        tok_idx = torch.empty((M,), dtype=torch.int32, device=dev)
+        tok_val = torch.empty((M,), dtype=torch.float32, device=dev)
 
         def token(s):
             x = x0
@@ -300,10 +304,22 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
                     q = L[kind][i]
                     w4.gemm(q[0], q[1], q[2], xa, y=ya, workspace=wk_sq, stream=s)
                 x = nx
-            w4.gemm(head[0], head[1], head[2], x, y=logits, workspace=wk_hd, stream=s)
+            # greedy decoding: the head's argmax, without materialising logits
+            w4.gemm_argmax(head[0], head[1], head[2], x, idx=tok_idx, val=tok_val, workspace=wk_hd,
+                           stream=s)
 
         t = graph_time([token], replays, stream)
+        t_head = graph_time([lambda s: w4.gemm(head[0], head[1], head[2], x0, y=logits, workspace=wk_hd0,
+                                               stream=s)] * 8, replays, stream)
+        t_head_am = graph_time([lambda s: w4.gemm_argmax(head[0], head[1], head[2], x0, idx=tok_idx, val=tok_val,
+                                                         workspace=wk_hd, stream=s)] * 8, replays, stream)
+        bh = weight_bytes(V, H)
+        out[f"head_M{M}"] = dict(us_per_call=t_head * 1e6, gbs=bh / t_head / 1e9,
+                                 argmax_us_per_call=t_head_am * 1e6, argmax_gbs=bh / t_head_am / 1e9)
+        log(f"[bench] head 5120->{V} M={M}: logits {t_head*1e6:.1f} us ({bh/t_head/1e9:.0f} GB/s), "
+            f"fused argmax {t_head_am*1e6:.1f} us ({bh/t_head_am/1e9:.0f} GB/s)")
         out[f"tower_M{M}"] = dict(ms_per_token=t * 1e3, tokens_per_s=1.0 / t, launches_per_token=6 * layers + 1,
+                                  head="fused greedy argmax",
                                   bytes_per_token=b_token, gbs=b_token / t / 1e9,
                                   pct_peak=100 * b_token / t / 1e9 / HBM_PEAK_GBS)
         log(f"[bench] tower M={M}: {t*1e3:.3f} ms/token ({1/t:.1f} tok/s), {b_token/t/1e9:.0f} GB/s "
