@@ -737,32 +737,51 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
       }
     }
   };
-  // x -> LDS: rows 0..4P-1 (rows >= M are zero), 16 B pad per row; ring
-  // slot 0, the x loads, the rest of the weight prologue, then the LDS stores
-  constexpr int XMAX = LB > 512 ? 8 : 16;
-  uint4 xr[XMAX];
-  auto xpos = [](int cu) { return cu; };
-#ifndef W4A16_WEIGHTS_FIRST
-  // ring slot 0 first: the weight stream starts as early in the (cold)
-  // instruction stream as possible, and the first step needs it anyway
-  issue(0);
-  x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
-#pragma unroll
-  for (int d = 1; d < D; ++d) issue(d);
-#else
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue(d);
-#endif
-  // (issue is unconditional: a wave without steps loads its clamped start
-  // position)
-  W4A16_STAMP(t_issued);
+  // x -> LDS: rows 0..4P-1 (rows >= M are zero), 16 B pad per row.
   const float gv0 = load_f32_vmem(a.g0);
   const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
   if (lane == 0) wft[wv] = T > 0 ? ft : kNoTask;
-#ifdef W4A16_WEIGHTS_FIRST
-  x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
-#endif
-  x_stage_store(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, CRS << 2, a.rUPR, RSU, tid, NT, xpos);
+  const int upr = CRS << 2;  // 16-byte x units per row of the slice
+  if ((upr & 63) == 0) {
+    // Direct-to-LDS path (every row of the slice is whole 64-unit blocks):
+    // the weight prologue first, then one 1 KiB direct-to-LDS load per block
+    // of 64 units (a short rolled loop: the launch starts with a cold
+    // instruction cache, and a long unrolled staging sequence kept the
+    // weight stream waiting), zeros for the padding rows, and one wait for
+    // everything before the barrier.
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d);
+    W4A16_STAMP(t_issued0);
+    const int cpr = upr >> 6;                    // 64-unit blocks per row
+    const float rcpr = 64.0f * a.rUPR;           // = fp32(1 / cpr), exactly
+    const int nblk = (a.M < 4 * P ? a.M : 4 * P) * cpr;
+    const uint4* xg = reinterpret_cast<const uint4*>(a.x) + (c0 << 2) + lane;
+    for (int j = wv; j < nblk; j += W) {
+      const int m = div_small(j, cpr, rcpr), cb = j - m * cpr;
+      __builtin_amdgcn_global_load_lds(
+          xg + (size_t)m * (K >> 3) + cb * 64,
+          (__attribute__((address_space(3))) void*)(xs + m * RSU + cb * 64), 16, 0, 0);
+    }
+    for (int u = a.M * RSU + tid; u < 4 * P * RSU; u += NT) xs[u] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads have landed
+    (void)t_issued0;
+  } else {
+    // register path: ring slot 0 first (the weight stream starts as early
+    // in the cold instruction stream as possible), the x loads, the rest of
+    // the prologue, then the LDS stores (loads complete in order, so the
+    // stores wait for slot 0 and x only)
+    constexpr int XMAX = LB > 512 ? 8 : 16;
+    uint4 xr[XMAX];
+    auto xpos = [](int cu) { return cu; };
+    issue(0);
+    x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, upr, a.rUPR, tid, NT);
+#pragma unroll
+    for (int d = 1; d < D; ++d) issue(d);
+    x_stage_store(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, upr, a.rUPR, RSU, tid, NT, xpos);
+  }
+  // (issue is unconditional: a wave without steps loads its clamped start
+  // position)
+  W4A16_STAMP(t_issued);
   __syncthreads();
   W4A16_STAMP(t_barrier);
 #ifdef W4A16_TRACE
