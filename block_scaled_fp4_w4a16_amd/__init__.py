@@ -26,7 +26,7 @@ __all__ = ["gemm", "gemm_gate_up_swiglu", "gemm_argmax", "dequant", "quantize", 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libw4a16.so")
 _lib = None
-MAX_M = 16
+MAX_M = 32
 
 OK, ERR_INVALID_VALUE, ERR_UNSUPPORTED, ERR_LAUNCH = 0, 1, 2, 3
 

@@ -88,13 +88,17 @@ struct KernEntry {
 #define W4A16_MFMA_SET(F)                                                          \
   W4A16_MFMA_ALL_P(1, 8, F, 512) W4A16_MFMA_ALL_P(1, 16, F, 512)                   \
   W4A16_MFMA_ALL_P(2, 4, F, 512) W4A16_MFMA_ALL_P(2, 8, F, 512)                    \
-  W4A16_MFMA_ALL_P(2, 8, F, 1024) W4A16_MFMA_ALL_P(4, 4, F, 512)
+  W4A16_MFMA_ALL_P(2, 8, F, 1024) W4A16_MFMA_ALL_P(4, 4, F, 512)                   \
+  W4A16_ME(5, 1, 4, F, 512) W4A16_ME(6, 1, 4, F, 512) W4A16_ME(7, 1, 4, F, 512)     \
+  W4A16_ME(8, 1, 4, F, 512)
 #endif
 // the launch rules' variants (the argmax epilogue exists only in these)
 #define W4A16_VALU_BASE(F)                                                         \
   W4A16_VALU_ALL_MT(8, 4, F, 1024) W4A16_VALU_ALL_MT(16, 4, F, 1024)               \
   W4A16_VALU_ALL_MT(32, 4, F, 1024)
-#define W4A16_MFMA_BASE(F) W4A16_MFMA_ALL_P(2, 4, F, 512)
+#define W4A16_MFMA_BASE(F)                                                         \
+  W4A16_MFMA_ALL_P(2, 4, F, 512) W4A16_ME(5, 1, 4, F, 512) W4A16_ME(6, 1, 4, F, 512)     \
+  W4A16_ME(7, 1, 4, F, 512) W4A16_ME(8, 1, 4, F, 512)
 #ifndef W4A16_TUNING
 #define W4A16_VALU_SET(F) W4A16_VALU_BASE(F)
 #define W4A16_MFMA_SET(F) W4A16_MFMA_BASE(F)
@@ -159,7 +163,7 @@ Plan plan_gemm(int M, int N, int K, int epi) {
     wmax = 8;
     wg_per_cu = 1;
   } else {
-    pl.lr = 2;
+    pl.lr = M <= 16 ? 2 : 1;  // row quads per task (one above 16 rows: VGPRs)
     pl.LB = 512;
     wmax = 8;
     wg_per_cu = 1;
@@ -194,13 +198,19 @@ Plan plan_gemm(int M, int N, int K, int epi) {
               : (size_t)(64 / pl.lr) * M * (pl.lr < 16 ? 1 : pl.lr / 16);
   const size_t seg_vals = pl.mfma ? (size_t)pl.lr * ((M + 3) / 4) * 16 : (size_t)(64 / pl.lr) * M;
   const long long groups = ((long long)N + RT - 1) / RT;  // row groups in total
-  // smallest K split whose x slice, scratch and segment partials fit in LDS
-  // (VALU: whole chunk steps per lane)
+  // Smallest K split whose x slice, scratch and segment partials fit in LDS
+  // (VALU: whole chunk steps per lane) with one row block per CU and split.
+  // Only when no split fits that way (wide M: the x slice forces a split of
+  // few chunk steps per task, so each wave touches many tasks and their
+  // segment partials outgrow LDS) are 2, 4, 8 or 16 times as many row blocks
+  // tried, each with fewer tasks.
+  for (int grow = 1; grow <= 16; grow *= 2)
   for (int S = 1; S <= CR; ++S) {
     if (CR % S) continue;
     const int CRS = CR / S;
     if (!pl.mfma && CRS % pl.lr) continue;
     long long nrb = (long long)cus * wg_per_cu / S > 0 ? (long long)cus * wg_per_cu / S : 1;
+    nrb *= grow;
 #ifdef W4A16_TUNING
     if (ov && g_override.S > 0) {
       if (S != g_override.S) continue;
@@ -228,14 +238,16 @@ Plan plan_gemm(int M, int N, int K, int epi) {
     // the split is chosen for the largest wave count (so that it does not
     // depend on the occupancy query), the wave count then by occupancy
     const int Wfit = force_w ? wmax : (int)(TS < wmax ? TS : wmax);
-    if (lds_for(Wfit, nullptr) > kMaxLds && S < CR) continue;
+    if (lds_for(Wfit, nullptr) > kMaxLds) continue;
     const int W = force_w ? wmax : (int)(TS < wcap ? TS : wcap);
     long long kmax = 0;
     const size_t lds = lds_for(W, &kmax);
-    if (lds > kMaxLds && S < CR) continue;
+    if (lds > kMaxLds) continue;
     // quotients in the kernels (div_small) are exact below 2^23
     if (TS * (W + 1) >= (1LL << 23) || (long long)xrows * CRS * 4 + 1024LL * 16 >= (1LL << 23))
       return Plan{};
+    // argmax takes whole rows: no K split
+    if (epi == kEpiArgmax && S > 1) break;
     pl.S = S;
     pl.nrb = (int)nrb;
     pl.rq = rq;
@@ -244,9 +256,8 @@ Plan plan_gemm(int M, int N, int K, int epi) {
     pl.kmax = (int)kmax;
     pl.lds = lds;
     if (epi == kEpiArgmax) {
-      // argmax: no K split; the arrival counter, then one (value, index)
-      // candidate per workgroup and activation row
-      if (S > 1) return Plan{};
+      // argmax: the arrival counter, then one (value, index) candidate per
+      // workgroup and activation row
       pl.ws = kCounterBytes + (size_t)pl.nrb * (size_t)M * 2 * sizeof(float);
     } else {
       pl.ws = S > 1 ? kCounterBytes +
@@ -486,7 +497,7 @@ const char* w4a16_status_string(w4a16_status_t status) {
   switch (status) {
     case W4A16_OK: return "ok";
     case W4A16_ERR_INVALID_VALUE: return "invalid value (null pointer, non-positive size or short workspace)";
-    case W4A16_ERR_UNSUPPORTED: return "unsupported (M > 16, K % 256 != 0, misaligned pointer or shape too large)";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported (M > 32, K % 256 != 0, misaligned pointer or shape too large)";
     case W4A16_ERR_LAUNCH: return "kernel launch failed";
   }
   return "unknown status";

@@ -269,6 +269,31 @@ W4A16_DEV float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// p[0] + p[st] + ... + p[(S-1) st], added in that order; the loads of eight
+// slices are issued before the first of them is used (the partials live
+// beyond the XCD caches, so each load costs a far round trip).
+W4A16_DEV float splitk_sum(const float* p, size_t st, int S) {
+  float v = 0.0f;
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = load_coherent(p + (size_t)(s + j) * st);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += t[j];
+  }
+  if (s + 4 <= S) {
+    float t[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = load_coherent(p + (size_t)(s + j) * st);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v += t[j];
+    s += 4;
+  }
+  for (; s < S; ++s) v += load_coherent(p + (size_t)s * st);
+  return v;
+}
+
 template <bool FUSED>
 W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, float ig0,
                              float ig1) {
@@ -286,11 +311,9 @@ W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, fl
   for (int o = threadIdx.x; o < nrows * a.M; o += blockDim.x) {
     const int m = o / nrows, n = o - m * nrows;   // consecutive threads: consecutive rows
     const size_t i = (size_t)m * a.N + row_lo + n;
-    float v = 0.0f;
-    for (int s = 0; s < a.S; ++s) v += load_coherent(a.part + (size_t)s * MN + i);
+    const float v = splitk_sum(a.part + i, MN, a.S);
     if (FUSED) {
-      float u = 0.0f;
-      for (int s = 0; s < a.S; ++s) u += load_coherent(a.part + (size_t)(a.S + s) * MN + i);
+      const float u = splitk_sum(a.part + (size_t)a.S * MN + i, MN, a.S);
       a.y[i] = f32_to_bf16(silu(v * ig0) * (u * ig1));
     } else {
       a.y[i] = f32_to_bf16(v * ig0);
@@ -654,7 +677,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel, 4 <= M <= 16 (P = ceil(M/4) passes of 4 activation rows).
+// MFMA kernel, 4 <= M <= 32 (P = ceil(M/4) passes of 4 activation rows).
 //
 // Uses v_mfma_f32_4x4x4_16b_bf16: 16 independent 4x4x4 products per
 // instruction; lane l = 4*beta + j holds B[k=0..3][col j] and A[row j][k] of

@@ -16,8 +16,9 @@
  * 16-bit patterns (uint16_t).  All arrays are dense and row-major.
  *
  * Shapes: N = out_features, K = in_features (the reduction), M = number of
- * activation rows (tokens): M = 1 is single-token decode, M up to 16 covers a
- * speculative verify block (e.g. 6 drafts + 1).
+ * activation rows (tokens): M = 1 is single-token decode, M = 7 a speculative
+ * verify block (6 drafts + 1); M up to 32 covers verify trees and batched
+ * clients, with each weight read once for all rows.
  *
  * Ownership: every pointer is device memory owned by the caller (any
  * allocator).  The library allocates nothing, frees nothing and keeps no
@@ -48,7 +49,7 @@ typedef enum {
   W4A16_OK = 0,
   /* null pointer, M/N/K <= 0, or workspace smaller than required */
   W4A16_ERR_INVALID_VALUE = 1,
-  /* M > 16, K % 256 != 0, a pointer not aligned as documented, or a shape
+  /* M > 32, K % 256 != 0, a pointer not aligned as documented, or a shape
    * too large for the kernels (N, K * 2 must fit in 31 bits) */
   W4A16_ERR_UNSUPPORTED = 2,
   /* the HIP launch failed (hipGetLastError after the launch) */
@@ -56,13 +57,13 @@ typedef enum {
 } w4a16_status_t;
 
 /* Largest M (activation rows) the matmul entry points accept. */
-#define W4A16_MAX_M 16
+#define W4A16_MAX_M 32
 
 /*
  * y[M][N] = bf16( x[M][K] * W^T ),  W dequantised from (wq, ws, g) as above,
  * accumulated in fp32, rounded once to bf16 (nearest even).
  *   wq, ws, x : 16-byte aligned;  g : 4-byte aligned;  y : 4-byte aligned.
- *   K % 256 == 0 (keeps every scale row 16-byte aligned).  1 <= M <= 16.
+ *   K % 256 == 0 (keeps every scale row 16-byte aligned).  1 <= M <= 32.
  *   workspace : device scratch of at least w4a16_workspace_size(M, N, K)
  *               bytes, 16-byte aligned (may be NULL when that size is 0).
  *               When the x slice a workgroup needs does not fit in LDS

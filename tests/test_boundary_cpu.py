@@ -72,7 +72,7 @@ def test_bad_sizes_rejected(lib, call):
     assert call(lib, N=0) == w4.ERR_INVALID_VALUE
     assert call(lib, K=0) == w4.ERR_INVALID_VALUE
     assert call(lib, M=-3) == w4.ERR_INVALID_VALUE
-    assert call(lib, M=17) == w4.ERR_UNSUPPORTED
+    assert call(lib, M=33) == w4.ERR_UNSUPPORTED
     assert call(lib, K=272) == w4.ERR_UNSUPPORTED      # multiple of 16 but not of 256
     assert call(lib, K=128) == w4.ERR_UNSUPPORTED
 
@@ -97,7 +97,7 @@ def test_workspace_sizes(lib):
         size = (w4.workspace_size_gate_up if fused else w4.workspace_size)(M, N, K)
         S, counters = divmod(size - 4096, M * N * 4 * (2 if fused else 1))
         assert S >= 2 and counters == 0, (M, N, K, size)
-    assert w4.workspace_size(17, 64, 256) == 0            # unsupported shape: 0
+    assert w4.workspace_size(33, 64, 256) == 0            # unsupported shape: 0
 
 
 def test_short_workspace_rejected(lib):
@@ -156,6 +156,8 @@ def test_argmax_argument_checks(lib):
         assert call(**{arg: 0}) == w4.ERR_INVALID_VALUE, arg
     assert call(work=0, wbytes=0) == w4.ERR_INVALID_VALUE     # the workspace is always required
     assert call(idx=P + 2) == w4.ERR_UNSUPPORTED
-    assert call(M=17) == w4.ERR_UNSUPPORTED
+    assert call(M=33) == w4.ERR_UNSUPPORTED
+    assert w4.workspace_size_argmax(13, 1000, 5120) == 0       # 13 x rows of 5120 need a K split
+    assert w4.workspace_size_argmax(12, 1000, 5120) > 0
     assert w4.workspace_size_argmax(1, 248320, 5120) >= 4096 + 8
     assert w4.workspace_size_argmax(16, 64, 17408) == 0        # would need a K split

@@ -49,7 +49,8 @@ def check_valid(idx, val, ref, a, ctx):
             assert i == top[0], f"{ctx} row {m}: clear winner {top[0]}, got {i}"
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 20000, 5120), (7, 20000, 5120), (3, 1003, 1280), (13, 777, 2048)])
+@pytest.mark.parametrize("M,N,K", [(1, 20000, 5120), (7, 20000, 5120), (3, 1003, 1280), (13, 777, 2048),
+                                   (12, 3001, 5120), (32, 515, 1024)])
 def test_random_heads(M, N, K):
     wq, ws, g = synth.nvfp4_weights(70 + M, N, K)
     x = synth.activations(80 + M, M, K)

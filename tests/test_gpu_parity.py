@@ -177,14 +177,14 @@ def test_down_config(M):
 
 # ---- every M, ragged shapes, edge cases ---------------------------------------
 
-@pytest.mark.parametrize("M", list(range(1, 17)))
+@pytest.mark.parametrize("M", list(range(1, 33)))
 def test_every_m_ragged_n(M):
     N, K = 1003, 1280      # N not a multiple of any row group; K/32 = 40 chunks
     wq, ws, g = weights(100, N, K)
     check_gemm(wq, ws, g, synth.activations(200 + M, M, K), M, N, K, f"ragged M={M}")
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 7, 16, 17, 32])
 def test_fused_every_family_ragged_n(M):
     N, K = 777, 768
     wg, wu = weights(101, N, K), weights(102, N, K)
@@ -192,7 +192,8 @@ def test_fused_every_family_ragged_n(M):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 256), (16, 1, 256), (3, 2, 256), (5, 3, 512), (16, 5, 256),
-                                   (16, 64, 8192), (16, 33, 17408), (2, 7, 33024)])
+                                   (16, 64, 8192), (16, 33, 17408), (2, 7, 33024), (32, 1, 256),
+                                   (32, 64, 17408), (20, 33, 5120), (25, 640, 5120)])
 def test_small_and_extreme_shapes(M, N, K):
     wq, ws, g = weights(7 + N, N, K)
     check_gemm(wq, ws, g, synth.activations(M * 1000 + N, M, K), M, N, K, "shape")
@@ -267,7 +268,8 @@ def test_run_to_run_bitwise(M, N, K):
     assert all(torch.equal(ys[0], t) for t in ys[1:])
 
 
-@pytest.mark.parametrize("family,Ms", [("valu", (1, 2, 3)), ("mfma", (4, 5, 8))])
+@pytest.mark.parametrize("family,Ms", [("valu", (1, 2, 3)), ("mfma", (4, 5, 8)),
+                                       ("mfma one quad per task", (17, 21, 24))])
 def test_rows_do_not_depend_on_m_within_a_kernel_family(family, Ms):
     N, K = 300, 5120
     wq, ws, g = weights(16, N, K)
@@ -283,7 +285,7 @@ def test_rows_do_not_depend_on_m_within_a_kernel_family(family, Ms):
 def test_unsupported_shapes_raise():
     wq, ws, g = weights(18, 16, 256)
     with pytest.raises(w4.W4A16Error) as e:
-        w4.gemm(d_u8(wq), d_u8(ws), d_g(g), d_bf16(synth.activations(1, 17, 256)))
+        w4.gemm(d_u8(wq), d_u8(ws), d_g(g), d_bf16(synth.activations(1, 33, 256)))
     assert e.value.status == w4.ERR_UNSUPPORTED
 
 
