@@ -90,14 +90,14 @@ struct KernEntry {
   W4A16_MFMA_ALL_P(2, 4, F, 512) W4A16_MFMA_ALL_P(2, 8, F, 512)                    \
   W4A16_MFMA_ALL_P(2, 8, F, 1024) W4A16_MFMA_ALL_P(4, 4, F, 512)                   \
   W4A16_ME(5, 1, 4, F, 512) W4A16_ME(6, 1, 4, F, 512) W4A16_ME(7, 1, 4, F, 512)     \
-  W4A16_ME(8, 1, 4, F, 512)
+  W4A16_ME(8, 1, 4, F, 512) W4A16_MFMA_ALL_P(1, 4, F, 512)
 #endif
 // the launch rules' variants (the argmax epilogue exists only in these)
 #define W4A16_VALU_BASE(F)                                                         \
   W4A16_VALU_ALL_MT(8, 4, F, 1024) W4A16_VALU_ALL_MT(16, 4, F, 1024)               \
   W4A16_VALU_ALL_MT(32, 4, F, 1024)
 #define W4A16_MFMA_BASE(F)                                                         \
-  W4A16_MFMA_ALL_P(2, 4, F, 512) W4A16_ME(5, 1, 4, F, 512) W4A16_ME(6, 1, 4, F, 512)     \
+  W4A16_MFMA_ALL_P(1, 4, F, 512) W4A16_ME(5, 1, 4, F, 512) W4A16_ME(6, 1, 4, F, 512)     \
   W4A16_ME(7, 1, 4, F, 512) W4A16_ME(8, 1, 4, F, 512)
 #ifndef W4A16_TUNING
 #define W4A16_VALU_SET(F) W4A16_VALU_BASE(F)
@@ -154,7 +154,7 @@ Plan plan_gemm(int M, int N, int K, int epi) {
   // shallow rings (4 chunk loads in flight per lane); one workgroup of 8
   // waves per CU (x is staged into LDS once per workgroup, so fewer row
   // blocks means less x traffic); VALU rows read by 16 lanes; MFMA tasks of
-  // 2 row quads.
+  // one row quad (finer stream-K tasks beat two quads sharing x reads).
   pl.D = 4;
   int wmax, wg_per_cu;
   if (!pl.mfma) {
@@ -163,7 +163,7 @@ Plan plan_gemm(int M, int N, int K, int epi) {
     wmax = 8;
     wg_per_cu = 1;
   } else {
-    pl.lr = M <= 16 ? 2 : 1;  // row quads per task (one above 16 rows: VGPRs)
+    pl.lr = 1;  // row quads per task
     pl.LB = 512;
     wmax = 8;
     wg_per_cu = 1;
