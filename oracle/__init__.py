@@ -72,6 +72,10 @@ def _bind(path):
     lib.nvfp4_oracle_gate_up_swiglu.restype = None
     lib.nvfp4_oracle_quantize.argtypes = [P, I, I, P, P, P]
     lib.nvfp4_oracle_quantize.restype = None
+    lib.nvfp4_oracle_bf16_rne.argtypes = [ctypes.c_double]
+    lib.nvfp4_oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.nvfp4_oracle_bf16_rne_array.argtypes = [P, I, P]
+    lib.nvfp4_oracle_bf16_rne_array.restype = None
     lib.nvfp4_oracle_max_threads.argtypes = []
     lib.nvfp4_oracle_max_threads.restype = ctypes.c_int
     return lib
@@ -197,6 +201,25 @@ def gate_up_swiglu(wq_g, ws_g, g_g, wq_u, ws_u, g_u, x_bf16_bits, M, N, K, nthre
     return out
 
 
+def bf16_rne(v) -> np.ndarray:
+    """fp64 values -> bf16 bit patterns (uint16), nearest, ties to even."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().nvfp4_oracle_bf16_rne_array(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def mlp_swiglu(gate, up, down, x_bf16_bits, M, H, F, nthreads: int = 1):
+    """The MLP block: h = bf16(silu(x Wg^T) * (x Wu^T)) [M][F], then
+    y = h Wd^T [M][H] in fp64.  gate, up, down: (wq, ws, g); Wg, Wu are
+    [F][H], Wd is [H][F].  Returns dict with y, a (sum |h w|), h (exact
+    fp64 silu(gate)*up), h_bits (bf16 of h) and the gate/up dict."""
+    r = gate_up_swiglu(*gate, *up, x_bf16_bits, M, F, H, nthreads=nthreads)
+    h_bits = bf16_rne(r["y"])
+    y, a = gemm(*down, h_bits, M, H, F, nthreads=nthreads)
+    return dict(y=y, a=a, h=r["y"], h_bits=h_bits, gate_up=r)
+
+
 def quantize(w_f32, N, K):
     """NVFP4-encode fp32 W [N][K]: returns (wq u8 [N][K/2], ws u8 [N][K/16], g fp32)."""
     w = _c(w_f32, np.float32).reshape(N, K)
@@ -218,6 +241,19 @@ def max_threads() -> int:
 def gemm_bound(a):
     """Allowed |y_gpu - y_ref| for the plain matmul: 1e-2 * sum|x w| + 1e-6."""
     return 1e-2 * np.asarray(a) + 1e-6
+
+
+def mlp_bound(out, down_abs):
+    """Allowed |y_gpu - y_ref| for the MLP block.  With B the gate/up bound on
+    |h_gpu - h| (h exact), the oracle's h_bits within 2^-9 |h| of h, and the
+    matmul bound on the down projection of h_gpu:
+        1e-2 * sum_k |h_gpu| |w| + sum_k |w| |h_gpu - h_bits| + 1e-6
+     <= sum_k |w_k| * ((1 + 1e-2) B_k + (1e-2 + 2^-9) |h_k|) + 1e-6.
+    down_abs: |Wd| in fp64, [H][F]."""
+    r = out["gate_up"]
+    b = swiglu_bound(r["gate"], r["up"], r["a_gate"], r["a_up"])
+    c = (1.0 + 1e-2) * b + (1e-2 + 2.0 ** -9) * np.abs(out["h"])
+    return c @ np.asarray(down_abs).T + 1e-6
 
 
 def swiglu_bound(gate, up, a_gate, a_up):

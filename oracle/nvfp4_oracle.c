@@ -197,6 +197,36 @@ EXPORT void nvfp4_oracle_gate_up_swiglu(const uint8_t* wq_g, const uint8_t* ws_g
   (void)nthreads;
 }
 
+/* ---- the MLP block: h = bf16(silu(gate) * up), then the down projection -- */
+
+/* The bf16 value nearest to v, ties to the even significand, as its bit
+ * pattern (IEEE round-to-nearest-even into 1 sign, 8 exponent, 7 fraction
+ * bits): normal results keep 8 significant bits, results below 2^-126 are
+ * multiples of 2^-133 (subnormals), magnitudes that round beyond the largest
+ * finite value (2 - 2^-7) * 2^127 give infinity, NaN gives 0x7FC0.  The MLP
+ * hands h to the down projection in bf16, as a two-kernel pipeline would
+ * (the activations of the matmul are bf16 by the "W4A16" format). */
+EXPORT uint16_t nvfp4_oracle_bf16_rne(double v) {
+  if (isnan(v)) return 0x7FC0;
+  const uint16_t sign = signbit(v) ? 0x8000 : 0;
+  const double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);                                /* a = f * 2^e, f in [0.5, 1) */
+  const int qe = (e - 1 >= -126) ? e - 8 : -133; /* exponent of one unit in the last place */
+  const double r = nearbyint(ldexp(a, -qe));   /* exact scaling; ties to even */
+  const double rv = ldexp(r, qe);
+  if (rv > ldexp(255.0, 120)) return sign | 0x7F80; /* beyond (2 - 2^-7) * 2^127 */
+  const float f = (float)rv;                   /* exact: at most 8 significant bits */
+  uint32_t bits;
+  memcpy(&bits, &f, sizeof bits);
+  return (uint16_t)(sign | ((bits >> 16) & 0x7FFF));
+}
+
+EXPORT void nvfp4_oracle_bf16_rne_array(const double* v, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = nvfp4_oracle_bf16_rne(v[i]);
+}
+
 /* ---- quantiser (the encoding that produces the three tensors) ------------ */
 
 /* Nearest E4M3FN code to a non-negative value, ties to the even code,

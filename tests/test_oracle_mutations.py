@@ -35,6 +35,13 @@ PLANTS = [
      "double t = bf16_to_double(x[k]) * weight_at(wq, ws, gd, K, n, k);\n        acc += t;\n        mag += fabs(t);\n      }\n      y[m * N + n] = acc;"),
 ]
 
+PLANTS += [
+    ("bf16 rounding truncates", "const double r = nearbyint(ldexp(a, -qe));",
+     "const double r = floor(ldexp(a, -qe));"),
+    ("bf16 keeps 9 bits", "const int qe = (e - 1 >= -126) ? e - 8 : -133;",
+     "const int qe = (e - 1 >= -126) ? e - 9 : -133;"),
+]
+
 PIN_TESTS = [
     pins.test_e2m1_matches_ocp_table,
     pins.test_e4m3_matches_torch_all_codes,
@@ -42,6 +49,8 @@ PIN_TESTS = [
     pins.test_gemm_hand_example,
     lambda: pins.test_gemm_bruteforce_exact(2, 3, 32, 1),
     lambda: pins.test_gemm_bruteforce_exact(3, 4, 64, 2),
+    pins.test_bf16_rne_matches_torch_cast,
+    pins.test_mlp_bruteforce,
 ]
 
 

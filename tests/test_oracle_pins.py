@@ -412,3 +412,84 @@ def test_synth_encoder_agrees_with_oracle_quantizer():
         a = synth.encode_nvfp4(w)
         b = oracle.quantize(w, N, K)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]) and a[2] == b[2]
+
+
+# ---- MLP block: bf16 rounding of h, then the down projection -------------------
+
+def test_bf16_rne_matches_torch_cast():
+    # fp32-representable inputs, so torch's fp32 -> bf16 cast (round to nearest
+    # even) is a single rounding and serves as the reference
+    rng = np.random.default_rng(21)
+    v = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 20000),
+        # exact ties: 1 + (2j+1) 2^-8 lies halfway between two bf16 values
+        (1.0 + (2 * np.arange(64) + 1) * 2.0 ** -8).astype(np.float32),
+        -(3.0 + (2 * np.arange(64) + 1) * 2.0 ** -7).astype(np.float32),
+        # subnormal bf16 range, around the smallest normal, and near overflow
+        (np.arange(1, 300) * 2.0 ** -140).astype(np.float32),
+        np.float32([2.0 ** -126, 2.0 ** -126 * (1 - 2.0 ** -9), 3.389e38, 3.3962e38, 3.4e38,
+                    -3.4e38, 0.0, -0.0]),
+    ]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_rne(v.astype(np.float64))
+    assert np.array_equal(got, ref)
+    assert oracle.bf16_rne(np.array([np.nan]))[0] & 0x7FFF > 0x7F80   # NaN stays NaN
+
+
+def _py_bf16(v):
+    """Nearest bf16 value (ties to even) of a normal-range float, pure Python."""
+    if v == 0.0:
+        return 0.0
+    f, e = math.frexp(abs(v))                     # |v| = f 2^e, f in [0.5, 1)
+    r = round(f * 256) / 256                      # round() on an exact binary value: ties to even
+    return math.copysign(math.ldexp(r, e), v)
+
+
+def test_mlp_bruteforce():
+    # independent re-derivation on a tiny block: exact rational gate/up from
+    # the golden tables, silu in Python floats, h rounded to bf16 in pure
+    # Python, then the down projection as exact rationals
+    M, H, F = 2, 32, 16
+    rng = np.random.default_rng(8)
+    def w(n, k, seed):
+        r = np.random.default_rng(seed)
+        wq = r.integers(0, 256, (n, k // 2), dtype=np.uint8)
+        ws = r.integers(0x28, 0x48, (n, k // 16), dtype=np.uint8)
+        return wq, ws, np.float32(r.uniform(1.0, 8.0))
+    gate, up, down = w(F, H, 1), w(F, H, 2), w(H, F, 3)
+    x = synth.bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    out = oracle.mlp_swiglu(gate, up, down, x, M, H, F)
+    yg, _ = _frac_gemm(*gate, x, M, F, H)
+    yu, _ = _frac_gemm(*up, x, M, F, H)
+    h = np.zeros((M, F))
+    for m in range(M):
+        for n in range(F):
+            a, b = float(yg[m][n]), float(yu[m][n])
+            h[m, n] = _py_bf16(a / (1.0 + math.exp(-a)) * b)
+    hb = synth.bf16_bits(h.astype(np.float32))
+    assert np.array_equal(out["h_bits"], hb)
+    yd, ad = _frac_gemm(*down, hb, M, H, F)
+    for m in range(M):
+        for n in range(H):
+            A = float(ad[m][n])
+            assert abs(out["y"][m, n] - float(yd[m][n])) <= 1e-12 * A + 1e-300
+            assert abs(out["a"][m, n] - A) <= 1e-12 * A
+
+
+def test_mlp_bound_covers_perturbed_h():
+    # any h_gpu within the gate/up bound of h, pushed through the down
+    # projection with the matmul error at its limit, stays inside mlp_bound
+    M, H, F = 3, 64, 48
+    rng = np.random.default_rng(4)
+    gate, up, down = (synth.nvfp4_weights(s, n, k) for s, n, k in ((31, F, H), (32, F, H), (33, H, F)))
+    x = synth.bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+    out = oracle.mlp_swiglu(gate, up, down, x, M, H, F)
+    wd = oracle.dequant_f64(*down, H, F)
+    bound = oracle.mlp_bound(out, np.abs(wd))
+    r = out["gate_up"]
+    bh = oracle.swiglu_bound(r["gate"], r["up"], r["a_gate"], r["a_up"])
+    for sign in (-1.0, 1.0):
+        h_gpu = out["h"] + sign * bh * np.sign(wd.sum(axis=0))[None, :]
+        y_gpu = h_gpu @ wd.T
+        y_gpu += sign * 1e-2 * (np.abs(h_gpu) @ np.abs(wd).T)
+        assert np.all(np.abs(y_gpu - out["y"]) <= bound)
