@@ -7,9 +7,11 @@ Default workload (one JSON line on stdout): the square projection, K = N =
 scales + 4 B g) per call / time per call, plus % of the 8 TB/s HBM peak.
 
 `--extra` also times the fused gate/up (M = 1, 7) and down (M = 1, 2, 4, 7,
-8) configurations, and `--tower` the full-tower decode sweep (64 layers of
-gate/up + SwiGLU, down and q/k/v/o plus the 248320-wide head, one HIP graph
-replay per token, M = 1 and 7); both report under "extra" in the same line.
+8) configurations and the whole MLP block (gate/up + SwiGLU + down, one
+persistent launch vs two launches, M = 1, 7), and `--tower` the full-tower
+decode sweep (64 layers of the MLP block and q/k/v/o plus the 248320-wide
+head, one HIP graph replay per token, M = 1 and 7); both report under "extra"
+in the same line.
 
 The timed region brackets the calls with HIP events recorded on the stream
 the kernels run on; inputs are resident in HBM before timing starts.
@@ -219,7 +221,6 @@ def bench_extra(dev, stream, cycles=10):
         b = 2 * weight_bytes(N, K)
         out[f"gate_up_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
         log(f"[bench] gate_up M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
-    del G, U
     c = synth.CONFIGS["down"]
     N, K, copies = c["N"], c["K"], c["copies"]
     log(f"[bench] generating down K={K} N={N} x{copies}")
@@ -236,15 +237,40 @@ def bench_extra(dev, stream, cycles=10):
         b = weight_bytes(N, K)
         out[f"down_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
         log(f"[bench] down M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
+    # the whole MLP block (gate/up + SwiGLU + down) per call: one persistent
+    # launch, and the same calls forced to two launches
+    H, F = N, K          # the down projection's output and input widths
+    nb = min(len(G[0]), len(D[0]))
+    for M in (1, 7):
+        x = to_dev_bf16(synth.activations(synth.CONFIGS["gate_up"]["seed_x"], M, H), dev)
+        y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+        work = w4.new_workspace_mlp(M, H, F, dev)
+        fns = [lambda s, i=i: w4.mlp_swiglu((G[0][i], G[1][i], G[2][i]), (U[0][i], U[1][i], U[2][i]),
+                                            (D[0][i], D[1][i], D[2][i]), x, y=y, workspace=work, stream=s)
+               for i in range(nb)]
+        b = 2 * weight_bytes(F, H) + weight_bytes(H, F)
+        res = {"one_launch": w4.mlp_one_launch(M, H, F)}
+        for mode, name in ((0, "auto"), (1, "two_launches")):
+            w4.mlp_set_options(mode, 1 << 20)
+            try:
+                t = graph_time(fns, cycles, stream)
+            finally:
+                w4.mlp_set_options(0, 1 << 20)
+            res[name] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
+            log(f"[bench] mlp block M={M} ({name}): {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
+        out[f"mlp_M{M}"] = res
+    del G, U, D
     return out
 
 
 def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
     """Full-tower decode sweep, one token = one HIP graph replay of
-    `layers` x (fused gate/up + SwiGLU 5120 -> 2 x 17408, down 17408 -> 5120,
-    q, k, v, o 5120 -> 5120) followed by the 5120 -> 248320 head GEMV with
-    fused greedy argmax (the head alone is also timed with and without it): 385
-    launches and 14.1 GB of distinct weight allocations per token.  The MLP
+    `layers` x (the MLP block: gate/up + SwiGLU 5120 -> 2 x 17408 and down
+    17408 -> 5120, one persistent launch where the device allows it; q, k, v,
+    o 5120 -> 5120) followed by the 5120 -> 248320 head GEMV with fused greedy
+    argmax (the head alone is also timed with and without it): 321 launches
+    (385 with two-launch MLP blocks) and 14.1 GB of distinct weight
+    allocations per token.  The MLP
     chain is wired (SwiGLU output feeds down, down's output feeds the next
     layer's gate/up); q/k/v/o and the head read fixed synthetic activations
     (there is no attention).  Weights per layer are byte-identical replicas of
@@ -281,12 +307,10 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
     for M in Ms:
         x0 = to_dev_bf16(synth.activations(cg["seed_x"], M, H), dev)
         xa = to_dev_bf16(synth.activations(cs["seed_x"], M, H), dev)
-        h = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
         xs = [torch.empty((M, H), dtype=torch.bfloat16, device=dev) for _ in range(2)]
         ya = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
         logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
-        wk_gu = w4.new_workspace(M, F, H, dev, fused=True)
-        wk_dn = w4.new_workspace(M, H, F, dev)
+        wk_mlp = w4.new_workspace_mlp(M, H, F, dev)
         wk_sq = w4.new_workspace(M, H, H, dev)
         wk_hd0 = w4.new_workspace(M, V, H, dev)
         wk_hd = torch.zeros(w4.workspace_size_argmax(M, V, H), dtype=torch.uint8, device=dev)
@@ -296,10 +320,8 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
         def token(s):
             x = x0
             for i in range(layers):
-                g, u, d = L["gate"][i], L["up"][i], L["down"][i]
-                w4.gemm_gate_up_swiglu(g[0], g[1], g[2], u[0], u[1], u[2], x, y=h, workspace=wk_gu, stream=s)
                 nx = xs[i % 2]
-                w4.gemm(d[0], d[1], d[2], h, y=nx, workspace=wk_dn, stream=s)
+                w4.mlp_swiglu(L["gate"][i], L["up"][i], L["down"][i], x, y=nx, workspace=wk_mlp, stream=s)
                 for kind in ("q", "k", "v", "o"):
                     q = L[kind][i]
                     w4.gemm(q[0], q[1], q[2], xa, y=ya, workspace=wk_sq, stream=s)
@@ -318,7 +340,9 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
                                  argmax_us_per_call=t_head_am * 1e6, argmax_gbs=bh / t_head_am / 1e9)
         log(f"[bench] head 5120->{V} M={M}: logits {t_head*1e6:.1f} us ({bh/t_head/1e9:.0f} GB/s), "
             f"fused argmax {t_head_am*1e6:.1f} us ({bh/t_head_am/1e9:.0f} GB/s)")
-        out[f"tower_M{M}"] = dict(ms_per_token=t * 1e3, tokens_per_s=1.0 / t, launches_per_token=6 * layers + 1,
+        per_layer = 5 if w4.mlp_one_launch(M, H, F) == 1 else 6
+        out[f"tower_M{M}"] = dict(ms_per_token=t * 1e3, tokens_per_s=1.0 / t,
+                                  launches_per_token=per_layer * layers + 1,
                                   head="fused greedy argmax",
                                   bytes_per_token=b_token, gbs=b_token / t / 1e9,
                                   pct_peak=100 * b_token / t / 1e9 / HBM_PEAK_GBS)

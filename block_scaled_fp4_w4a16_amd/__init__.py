@@ -75,6 +75,14 @@ def lib():
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_abi_version.argtypes = []
     L.w4a16_abi_version.restype = I
+    L.w4a16_mlp_swiglu.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, P, Z, P]
+    L.w4a16_mlp_swiglu.restype = I
+    L.w4a16_workspace_size_mlp.argtypes = [I, I, I]
+    L.w4a16_workspace_size_mlp.restype = Z
+    L.w4a16_mlp_one_launch.argtypes = [I, I, I]
+    L.w4a16_mlp_one_launch.restype = I
+    L.w4a16_mlp_set_options.argtypes = [I, I]
+    L.w4a16_mlp_set_options.restype = I
     _lib = L
     return L
 
@@ -191,6 +199,65 @@ def gemm_gate_up_swiglu(wq_gate, ws_gate, g_gate, wq_up, ws_up, g_up, x, y=None,
                                          _ptr(workspace), wbytes, _stream(stream))
     if st != OK:
         raise W4A16Error(st, "w4a16_gemm_gate_up_swiglu")
+    return y
+
+
+# Byte offsets inside the MLP workspace (include/w4a16.h): h (bf16 [M][F]), the
+# barrier's generation word (any value) and its time-out flag.
+MLP_H_OFFSET = 10240
+MLP_GENERATION_OFFSET = 9344
+MLP_TIMEOUT_OFFSET = 9472
+
+
+def workspace_size_mlp(M: int, H: int, F: int) -> int:
+    return int(lib().w4a16_workspace_size_mlp(M, H, F))
+
+
+def mlp_one_launch(M: int, H: int, F: int) -> int:
+    """1: one persistent launch on the current device; 0: two launches; -1: unsupported."""
+    return int(lib().w4a16_mlp_one_launch(M, H, F))
+
+
+def mlp_set_options(mode: int = 0, spin_limit: int = 1 << 20) -> None:
+    """mode 0: one launch when possible, 1: always two; spin_limit: barrier polls."""
+    if lib().w4a16_mlp_set_options(int(mode), int(spin_limit)) != 1:
+        raise ValueError("invalid MLP options")
+
+
+def new_workspace_mlp(M: int, H: int, F: int, device):
+    """A zero-filled MLP workspace, reusable by calls made one after another."""
+    need = workspace_size_mlp(M, H, F)
+    if need == 0:
+        raise W4A16Error(ERR_UNSUPPORTED, "w4a16_workspace_size_mlp")
+    return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
+def mlp_swiglu(gate, up, down, x, y=None, workspace=None, stream=None):
+    """y[M, H] = bf16(bf16(silu(x @ Wg^T) * (x @ Wu^T)) @ Wd^T): one MLP block.
+    gate, up, down: (wq, ws, g) tuples; Wg, Wu are [F][H], Wd is [H][F]."""
+    F, H = _weights(*gate, "gate ")
+    if _weights(*up, "up ") != (F, H):
+        raise ValueError("gate and up weights must have the same shape")
+    if _weights(*down, "down ") != (H, F):
+        raise ValueError(f"down weights must be [{H}][{F}] (codes [{H}][{F // 2}])")
+    _check(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    if x.shape[1] != H:
+        raise ValueError(f"x has K={x.shape[1]}, gate/up weights have K={H}")
+    if y is None:
+        y = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    _check(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, H):
+        raise ValueError(f"y must be ({M}, {H})")
+    if workspace is None:
+        workspace = new_workspace_mlp(M, H, F, x.device) if M <= MAX_M else None
+    else:
+        _check(workspace, "workspace", workspace.dtype, None)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().w4a16_mlp_swiglu(*[_ptr(t) for t in (*gate, *up, *down)], _ptr(x), _ptr(y), M, H, F,
+                                _ptr(workspace), wbytes, _stream(stream))
+    if st != OK:
+        raise W4A16Error(st, "w4a16_mlp_swiglu")
     return y
 
 

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "w4a16_kernels.h"
+#include "w4a16_mlp.h"
 #include "w4a16_quant.h"
 
 namespace w4a16 {
@@ -301,13 +302,9 @@ size_t workspace_bytes_for(int M, int N, int K, int epi) {
   return plan_gemm(M, N, K, epi).ws;
 }
 
-w4a16_status_t run_matmul(MatArgs a, int epi, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
-  const Plan pl = plan_gemm(a.M, a.N, a.K, epi);
-  if (pl.S == 0 || pl.lds > kMaxLds) return W4A16_ERR_UNSUPPORTED;
-  if (workspace_bytes < pl.ws || (pl.ws > 0 && workspace == nullptr))
-    return W4A16_ERR_INVALID_VALUE;
-  if (pl.ws > 0 && !aligned(workspace, 16)) return W4A16_ERR_UNSUPPORTED;
+// Fill the plan-dependent launch arguments; cnt: the split-K arrival
+// counters, part: the fp32 partials (or argmax candidates).
+void prepare(MatArgs& a, const Plan& pl, int* cnt, float* part) {
   a.rq = pl.rq;
   a.rr = pl.rr;
   a.kmax = pl.kmax;
@@ -317,10 +314,145 @@ w4a16_status_t run_matmul(MatArgs a, int epi, void* workspace, size_t workspace_
   a.rW = 1.0f / (float)pl.W;
   a.rCPL = 1.0f / (float)cpl;
   a.rUPR = 1.0f / (float)(a.CRS * 4);
-  a.cnt = static_cast<int*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes);
-  a.cand = a.part;
+  a.cnt = cnt;
+  a.part = part;
+  a.cand = part;
+}
+
+w4a16_status_t run_matmul(MatArgs a, int epi, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  const Plan pl = plan_gemm(a.M, a.N, a.K, epi);
+  if (pl.S == 0 || pl.lds > kMaxLds) return W4A16_ERR_UNSUPPORTED;
+  if (workspace_bytes < pl.ws || (pl.ws > 0 && workspace == nullptr))
+    return W4A16_ERR_INVALID_VALUE;
+  if (pl.ws > 0 && !aligned(workspace, 16)) return W4A16_ERR_UNSUPPORTED;
+  prepare(a, pl, static_cast<int*>(workspace),
+          reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes));
   const hipError_t e = dispatch(pl, epi, stream, a);
+  return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+// ---- MLP block: gate/up + SwiGLU, then down ------------------------------------
+// Workspace: the two phases' split-K counters (4 KiB each), the barrier
+// words, h (bf16 [M][F]), then each phase's fp32 partials.
+constexpr size_t kMlpBarrierOffset = 2 * kCounterBytes;
+constexpr size_t kMlpHOffset = W4A16_MLP_H_OFFSET;
+static_assert(kMlpHOffset >= kMlpBarrierOffset + (kBarFlag + 32) * sizeof(int), "barrier words");
+static_assert(W4A16_MLP_TIMEOUT_OFFSET == kMlpBarrierOffset + kBarFlag * sizeof(int), "time-out flag");
+static_assert(W4A16_MLP_GENERATION_OFFSET == kMlpBarrierOffset + kBarGen * sizeof(int), "generation");
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct MlpKernEntry {
+  bool mfma;
+  int rows;    // VALU: MT; MFMA: P
+  int l1, l2;  // VALU: lanes per weight row of each phase (MFMA: 1, 1)
+  int D, LB;
+  const void* fn;
+};
+#define W4A16_MLPV(MT, L1, L2) \
+  {false, MT, L1, L2, 4, 1024, reinterpret_cast<const void*>(&k_mlp_valu<MT, L1, L2, 4, 1024>)},
+#define W4A16_MLPV_L(L1, L2) W4A16_MLPV(1, L1, L2) W4A16_MLPV(2, L1, L2) W4A16_MLPV(3, L1, L2)
+#define W4A16_MLPM(P) {true, P, 1, 1, 4, 512, reinterpret_cast<const void*>(&k_mlp_mfma<P, 4, 512>)},
+const MlpKernEntry kMlpKernels[] = {
+    W4A16_MLPV_L(16, 16) W4A16_MLPV_L(16, 8) W4A16_MLPV_L(8, 16) W4A16_MLPV_L(8, 8)
+    W4A16_MLPM(1) W4A16_MLPM(2) W4A16_MLPM(3) W4A16_MLPM(4)
+    W4A16_MLPM(5) W4A16_MLPM(6) W4A16_MLPM(7) W4A16_MLPM(8)};
+
+// Library options for the MLP entry point (diagnostics and tests).
+int g_mlp_mode = 0;            // 0: one launch when possible; 1: always two launches
+int g_mlp_spin = 1 << 20;      // barrier polls before a workgroup gives up
+
+struct MlpPlan {
+  Plan p1, p2;              // gate/up (N = F, K = H) and down (N = H, K = F)
+  const MlpKernEntry* k;    // persistent kernel, or nullptr: two launches
+  int grid;
+  size_t lds;
+  size_t part1, part2, ws;  // byte offsets of the partials, total bytes
+};
+
+MlpPlan plan_mlp(int M, int H, int F) {
+  MlpPlan mp{};
+  mp.p1 = plan_gemm(M, F, H, kEpiSwiglu);
+  mp.p2 = plan_gemm(M, H, F, kEpiPlain);
+  if (mp.p1.S == 0 || mp.p2.S == 0) return MlpPlan{};
+  const size_t h_bytes = align256((size_t)M * F * 2);
+  const size_t w1 = mp.p1.ws > 0 ? align256(mp.p1.ws - kCounterBytes) : 0;
+  const size_t w2 = mp.p2.ws > 0 ? align256(mp.p2.ws - kCounterBytes) : 0;
+  mp.part1 = kMlpHOffset + h_bytes;
+  mp.part2 = mp.part1 + w1;
+  mp.ws = mp.part2 + w2;
+  // one launch: both phases on the same kernel family, block size and ring
+  // depth, h addressable by 32-bit buffer offsets, and every workgroup of the
+  // grid resident at once (the barrier waits for all of them)
+  const Plan &a = mp.p1, &b = mp.p2;
+  if (g_mlp_mode != 0 || a.mfma != b.mfma || a.W != b.W || a.LB != b.LB || a.D != b.D ||
+      (size_t)M * F * 2 >= ((size_t)1 << 31))
+    return mp;
+  const int rows = a.mfma ? (M + 3) / 4 : M;
+  for (const MlpKernEntry& e : kMlpKernels)
+    if (e.mfma == a.mfma && e.rows == rows && e.D == a.D && e.LB == a.LB &&
+        (a.mfma || (e.l1 == a.lr && e.l2 == b.lr)) && (!a.mfma || (a.lr == 1 && b.lr == 1)))
+      mp.k = &e;
+  if (!mp.k) return mp;
+  const int nwg1 = a.nrb * a.S, nwg2 = b.nrb * b.S;
+  mp.grid = nwg1 > nwg2 ? nwg1 : nwg2;
+  mp.lds = a.lds > b.lds ? a.lds : b.lds;
+  return mp;
+}
+
+// Whether mp's persistent kernel can run with its whole grid resident (the
+// workgroups per CU that the occupancy query allows, times the CUs); clears
+// mp.k if not.  Needs the device.
+void mlp_check_resident(MlpPlan& mp) {
+  if (!mp.k) return;
+  if (mp.lds > 64 * 1024 &&
+      hipFuncSetAttribute(mp.k->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)mp.lds) !=
+          hipSuccess) {
+    mp.k = nullptr;
+    return;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mp.k->fn, mp.p1.W * 64, mp.lds) !=
+          hipSuccess ||
+      (long long)per_cu * cu_count() < mp.grid)
+    mp.k = nullptr;
+}
+
+w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  const int M = up0.M, H = up0.K, F = up0.N;
+  MlpPlan mp = plan_mlp(M, H, F);
+  if (mp.p1.S == 0 || mp.p1.lds > kMaxLds || mp.p2.lds > kMaxLds) return W4A16_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < mp.ws) return W4A16_ERR_INVALID_VALUE;
+  if (!aligned(workspace, 256)) return W4A16_ERR_UNSUPPORTED;
+  char* w = static_cast<char*>(workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(w + kMlpHOffset);
+  MatArgs up = up0, down = down0;
+  up.y = h;
+  down.x = h;
+  prepare(up, mp.p1, reinterpret_cast<int*>(w), reinterpret_cast<float*>(w + mp.part1));
+  prepare(down, mp.p2, reinterpret_cast<int*>(w + kCounterBytes),
+          reinterpret_cast<float*>(w + mp.part2));
+  mlp_check_resident(mp);
+  hipError_t e;
+  if (mp.k) {
+    MlpArgs m{};
+    m.up = up;
+    m.down = down;
+    m.nrb1 = mp.p1.nrb;
+    m.nwg1 = mp.p1.nrb * mp.p1.S;
+    m.nrb2 = mp.p2.nrb;
+    m.nwg2 = mp.p2.nrb * mp.p2.S;
+    m.bar = reinterpret_cast<int*>(w + kMlpBarrierOffset);
+    m.spin_limit = g_mlp_spin;
+    void* argv[] = {&m};
+    e = hipLaunchKernel(mp.k->fn, dim3((unsigned)mp.grid), dim3((unsigned)(mp.p1.W * 64)), argv,
+                        mp.lds, stream);
+    if (e == hipSuccess) e = hipGetLastError();
+  } else {
+    e = dispatch(mp.p1, kEpiSwiglu, stream, up);
+    if (e == hipSuccess) e = dispatch(mp.p2, kEpiPlain, stream, down);
+  }
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
@@ -491,6 +623,66 @@ w4a16_status_t w4a16_quantize_bf16(const uint16_t* w, uint8_t* wq, uint8_t* ws, 
                                    int K, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
   return run_quantize(w, wq, ws, g, N, K, workspace, workspace_bytes, stream);
+}
+
+w4a16_status_t w4a16_mlp_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,
+                                const float* g_gate, const uint8_t* wq_up, const uint8_t* ws_up,
+                                const float* g_up, const uint8_t* wq_down, const uint8_t* ws_down,
+                                const float* g_down, const uint16_t* x, uint16_t* y, int M, int H,
+                                int F, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (!wq_gate || !ws_gate || !g_gate || !wq_up || !ws_up || !g_up || !wq_down || !ws_down ||
+      !g_down || !x || !y)
+    return W4A16_ERR_INVALID_VALUE;
+  w4a16_status_t st = check_shape(M, F, H);
+  if (st != W4A16_OK) return st;
+  st = check_shape(M, H, F);
+  if (st != W4A16_OK) return st;
+  if (!aligned(wq_gate, 16) || !aligned(ws_gate, 16) || !aligned(wq_up, 16) ||
+      !aligned(ws_up, 16) || !aligned(wq_down, 16) || !aligned(ws_down, 16) || !aligned(x, 16) ||
+      !aligned(g_gate, 4) || !aligned(g_up, 4) || !aligned(g_down, 4) || !aligned(y, 4))
+    return W4A16_ERR_UNSUPPORTED;
+  MatArgs up{}, down{};
+  up.wq0 = wq_gate;
+  up.ws0 = ws_gate;
+  up.g0 = g_gate;
+  up.wq1 = wq_up;
+  up.ws1 = ws_up;
+  up.g1 = g_up;
+  up.x = x;
+  up.M = M;
+  up.N = F;
+  up.K = H;
+  down.wq0 = wq_down;
+  down.ws0 = ws_down;
+  down.g0 = g_down;
+  down.y = y;
+  down.M = M;
+  down.N = H;
+  down.K = F;
+  return run_mlp(up, down, workspace, workspace_bytes, stream);
+}
+
+size_t w4a16_workspace_size_mlp(int M, int H, int F) {
+  if (check_shape(M, F, H) != W4A16_OK || check_shape(M, H, F) != W4A16_OK) return 0;
+  const MlpPlan mp = plan_mlp(M, H, F);
+  if (mp.p1.S == 0 || mp.p1.lds > kMaxLds || mp.p2.lds > kMaxLds) return 0;
+  return mp.ws;
+}
+
+int w4a16_mlp_one_launch(int M, int H, int F) {
+  if (check_shape(M, F, H) != W4A16_OK || check_shape(M, H, F) != W4A16_OK) return -1;
+  MlpPlan mp = plan_mlp(M, H, F);
+  if (mp.p1.S == 0 || mp.p1.lds > kMaxLds || mp.p2.lds > kMaxLds) return -1;
+  mlp_check_resident(mp);
+  return mp.k ? 1 : 0;
+}
+
+int w4a16_mlp_set_options(int mode, int spin_limit) {
+  if (mode < 0 || mode > 1 || spin_limit < 0) return 0;
+  g_mlp_mode = mode;
+  g_mlp_spin = spin_limit;
+  return 1;
 }
 
 const char* w4a16_status_string(w4a16_status_t status) {

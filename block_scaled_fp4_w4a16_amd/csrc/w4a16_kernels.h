@@ -142,6 +142,32 @@ W4A16_DEV float load_f32_vmem(const float* g) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
 }
 
+// Coherence mode of a matmul body (template argument CO).  The persistent MLP
+// kernel's first phase writes h with stores that go through to the device's
+// point of coherence (the L2 caches of the eight XCDs are not coherent with
+// each other), and its second phase reads h back with loads served from
+// there, so that no XCD reads a stale copy.
+constexpr int kCoPlain = 0, kCoLoadX = 1, kCoStoreY = 2;
+constexpr int kCpolSc1 = 16;  // cache-policy bits of a memory instruction: device scope
+
+// 16 bytes at base[i]; with XC, read at device scope (buffer load, sc1).
+// The byte offset i * 16 must stay below 2^31.
+template <bool XC>
+W4A16_DEV uint4 load_x16(const uint4* base, size_t i) {
+  if (!XC) return base[i];
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(base), (short)0, 0x7fffffff, kBufferWord3);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)(i * 16), 0, kCpolSc1);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// y[i] = v; with YC, an agent-scope store (writes through to the device's
+// point of coherence).
+template <bool YC>
+W4A16_DEV void store_y(uint16_t* y, size_t i, uint16_t v) {
+  if (YC) __hip_atomic_store(y + i, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else y[i] = v;
+}
+
 // v + (v of another lane chosen by a DPP control; all lanes stay active)
 template <int CTRL>
 W4A16_DEV float dpp_add(float v) {
@@ -219,7 +245,7 @@ struct XUnits {
     cu = u - m * upr;
   }
 };
-template <int XMAX>
+template <bool XC, int XMAX>
 W4A16_DEV void x_stage_issue(uint4 (&xr)[XMAX], const uint16_t* x, int M, int rows, int K,
                              int u0, int upr, float rupr, int tid, int nthr) {
   const uint4* xg = reinterpret_cast<const uint4*>(x);
@@ -231,11 +257,11 @@ W4A16_DEV void x_stage_issue(uint4 (&xr)[XMAX], const uint16_t* x, int M, int ro
       const int u = tid + i * nthr;
       int m, cu;
       xu.split(u, m, cu);
-      if (u < xu.total && m < M) xr[i] = xg[(size_t)m * (K >> 3) + u0 + cu];
+      if (u < xu.total && m < M) xr[i] = load_x16<XC>(xg, (size_t)m * (K >> 3) + u0 + cu);
     }
   }
 }
-template <int XMAX, typename Pos>
+template <bool XC, int XMAX, typename Pos>
 W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[XMAX], const uint16_t* x, int M,
                              int rows, int K, int u0, int upr, float rupr, int RSU, int tid,
                              int nthr, Pos pos) {
@@ -253,7 +279,8 @@ W4A16_DEV void x_stage_store(uint4* xs, const uint4 (&xr)[XMAX], const uint16_t*
   for (int u = tid + XMAX * nthr; u < xu.total; u += nthr) {
     int m, cu;
     xu.split(u, m, cu);
-    xs[m * RSU + pos(cu)] = m < M ? xg[(size_t)m * (K >> 3) + u0 + cu] : make_uint4(0u, 0u, 0u, 0u);
+    xs[m * RSU + pos(cu)] =
+        m < M ? load_x16<XC>(xg, (size_t)m * (K >> 3) + u0 + cu) : make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -303,7 +330,7 @@ W4A16_DEV float splitk_sum(const float* p, size_t st, int S) {
   return v;
 }
 
-template <bool FUSED>
+template <bool FUSED, bool YC>
 W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, float ig0,
                              float ig1) {
   __shared__ int is_last;
@@ -323,9 +350,9 @@ W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, fl
     const float v = splitk_sum(a.part + i, MN, a.S);
     if (FUSED) {
       const float u = splitk_sum(a.part + (size_t)a.S * MN + i, MN, a.S);
-      a.y[i] = f32_to_bf16(silu(v * ig0) * (u * ig1));
+      store_y<YC>(a.y, i, f32_to_bf16(silu(v * ig0) * (u * ig1)));
     } else {
-      a.y[i] = f32_to_bf16(v * ig0);
+      store_y<YC>(a.y, i, f32_to_bf16(v * ig0));
     }
   }
 }
@@ -429,9 +456,10 @@ constexpr int kNoTask = 1 << 30;
 // (swizzled) and are read with 128-bit LDS loads; lanes of different slots
 // read the same x (broadcast).
 // ---------------------------------------------------------------------------
-template <int MT, int L, int D, int EPI, int LB>
-__global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
+template <int MT, int L, int D, int EPI, int LB, int CO>
+W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
   constexpr bool FUSED = EPI == kEpiSwiglu;
+  constexpr bool XC = (CO & kCoLoadX) != 0, YC = (CO & kCoStoreY) != 0;
   W4A16_STAMP(t_start);
   extern __shared__ uint4 xs[];
   constexpr int G = 64 / L;
@@ -443,7 +471,6 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.K, S = a.S, CRS = a.CRS;  // CRS: chunks per row in this K-slice
-  const int ks = blockIdx.y, rb = blockIdx.x;
   const int c0 = ks * CRS;               // first chunk of the slice
   const int CPL = CRS / L, RSU = (CRS << 2) + 1;
   const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
@@ -501,7 +528,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   // ring slot 0 first: the weight stream starts as early in the (cold)
   // instruction stream as possible, and the first step needs it anyway
   issue(0);
-  x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
+  x_stage_issue<XC>(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
 #pragma unroll
   for (int d = 1; d < D; ++d) issue(d);
 #else
@@ -515,9 +542,9 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
   const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
   if (lane == 0) wft[wv] = T > 0 ? ft : kNoTask;
 #ifdef W4A16_WEIGHTS_FIRST
-  x_stage_issue(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
+  x_stage_issue<XC>(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
 #endif
-  x_stage_store(xs, xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, RSU, tid, NT, xpos);
+  x_stage_store<XC>(xs, xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, RSU, tid, NT, xpos);
   __syncthreads();
   W4A16_STAMP(t_barrier);
 #ifdef W4A16_TRACE
@@ -647,7 +674,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
         store_coherent(c + 1, __int_as_float(bi));
       }
     }
-    argmax_finish(a, gridDim.x, red, W);
+    argmax_finish(a, nwg, red, W);
   } else
   for (int n = tid; n < nrows; n += NT) {
     const int t = n / RT, rt = n - t * RT;
@@ -672,17 +699,23 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
         store_coherent(a.part + ((size_t)ks * a.M + m) * a.N + row, v[m]);
         if (FUSED) store_coherent(a.part + ((size_t)(S + ks) * a.M + m) * a.N + row, u[m]);
       } else if (FUSED) {
-        a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v[m] * ig0) * (u[m] * ig1));
+        store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(silu(v[m] * ig0) * (u[m] * ig1)));
       } else {
-        a.y[(size_t)m * a.N + row] = f32_to_bf16(v[m] * ig0);
+        store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(v[m] * ig0));
       }
     }
   }
-  if (S > 1) splitk_finish<FUSED>(a, rb, row_lo, row_hi - row_lo, ig0, ig1);
+  if (S > 1) splitk_finish<FUSED, YC>(a, rb, row_lo, row_hi - row_lo, ig0, ig1);
 #ifdef W4A16_TRACE
   W4A16_STAMP(t_done);
   W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);
 #endif
+}
+
+// One matmul per launch: workgroup (rb, ks) = (blockIdx.x, blockIdx.y).
+template <int MT, int L, int D, int EPI, int LB>
+__global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
+  gemm_valu<MT, L, D, EPI, LB, kCoPlain>(a, blockIdx.x, blockIdx.y, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -702,9 +735,10 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 // 16 B = 256 contiguous bytes per row per load) and the x slice of activation
 // row 4*pp + j from LDS, which then feeds the MFMAs of all R quads.
 // ---------------------------------------------------------------------------
-template <int P, int R, int D, int EPI, int LB>
-__global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
+template <int P, int R, int D, int EPI, int LB, int CO>
+W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
   constexpr bool FUSED = EPI == kEpiSwiglu;
+  constexpr bool XC = (CO & kCoLoadX) != 0, YC = (CO & kCoStoreY) != 0;
   W4A16_STAMP(t_start);
   extern __shared__ uint4 xs[];
   constexpr int QS = FUSED ? 2 : 4;      // output rows per quad
@@ -715,7 +749,6 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.K, S = a.S, CRS = a.CRS;  // CRS: chunks per row in this K-slice
-  const int ks = blockIdx.y, rb = blockIdx.x;
   const int c0 = ks * CRS;
   const int CPL = (CRS + 15) >> 4, RSU = (CRS << 2) + 1;
   const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
@@ -792,7 +825,8 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
       const int m = div_small(j, cpr, rcpr), cb = j - m * cpr;
       __builtin_amdgcn_global_load_lds(
           xg + (size_t)m * (K >> 3) + cb * 64,
-          (__attribute__((address_space(3))) void*)(xs + m * RSU + cb * 64), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(xs + m * RSU + cb * 64), 16, 0,
+          XC ? kCpolSc1 : 0);
     }
     for (int u = a.M * RSU + tid; u < 4 * P * RSU; u += NT) xs[u] = make_uint4(0u, 0u, 0u, 0u);
     __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads have landed
@@ -806,10 +840,10 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
     uint4 xr[XMAX];
     auto xpos = [](int cu) { return cu; };
     issue(0);
-    x_stage_issue(xr, a.x, a.M, 4 * P, K, c0 << 2, upr, a.rUPR, tid, NT);
+    x_stage_issue<XC>(xr, a.x, a.M, 4 * P, K, c0 << 2, upr, a.rUPR, tid, NT);
 #pragma unroll
     for (int d = 1; d < D; ++d) issue(d);
-    x_stage_store(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, upr, a.rUPR, RSU, tid, NT, xpos);
+    x_stage_store<XC>(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, upr, a.rUPR, RSU, tid, NT, xpos);
   }
   // (issue is unconditional: a wave without steps loads its clamped start
   // position)
@@ -953,7 +987,7 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
         store_coherent(c + 1, __int_as_float(bi));
       }
     }
-    argmax_finish(a, gridDim.x, red, W);
+    argmax_finish(a, nwg, red, W);
   } else
   // item o = n * 4P + m (rows m >= M are skipped): a constant divisor
   for (int o = tid; o < nrows * 4 * P; o += NT) {
@@ -976,16 +1010,21 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
       store_coherent(a.part + ((size_t)ks * M + m) * a.N + row, v);
       if (FUSED) store_coherent(a.part + ((size_t)(S + ks) * M + m) * a.N + row, u);
     } else if (FUSED) {
-      a.y[(size_t)m * a.N + row] = f32_to_bf16(silu(v * ig0) * (u * ig1));
+      store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(silu(v * ig0) * (u * ig1)));
     } else {
-      a.y[(size_t)m * a.N + row] = f32_to_bf16(v * ig0);
+      store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(v * ig0));
     }
   }
-  if (S > 1) splitk_finish<FUSED>(a, rb, row_lo, row_hi - row_lo, ig0, ig1);
+  if (S > 1) splitk_finish<FUSED, YC>(a, rb, row_lo, row_hi - row_lo, ig0, ig1);
 #ifdef W4A16_TRACE
   W4A16_STAMP(t_done);
   W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);
 #endif
+}
+
+template <int P, int R, int D, int EPI, int LB>
+__global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
+  gemm_mfma<P, R, D, EPI, LB, kCoPlain>(a, blockIdx.x, blockIdx.y, gridDim.x);
 }
 
 // ---------------------------------------------------------------------------

@@ -162,6 +162,60 @@ w4a16_status_t w4a16_quantize_bf16(const uint16_t* w, uint8_t* wq, uint8_t* ws, 
                                    int K, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/*
+ * A decoder layer's MLP block in one call:
+ *   h[M][F] = bf16( silu(x * Wg^T) * (x * Wu^T) )   (as w4a16_gemm_gate_up_swiglu)
+ *   y[M][H] = bf16( h * Wd^T )                       (as w4a16_gemm)
+ * with Wg, Wu : [F][H] and Wd : [H][F] in the schema above (each with its own
+ * g), x : bf16 [M][H], y : bf16 [M][H].  Same alignment rules as w4a16_gemm
+ * for every matrix; H % 256 == 0 and F % 256 == 0; 1 <= M <= 32.
+ * The qwentin README lists a persistent-MLP GEMV among its kernels and sizes
+ * grids to one wave of multiprocessors ("How it works", "Performance"); here,
+ * when the two matmuls' launch plans allow it (same kernel family and block
+ * size) and the whole grid fits on the device at once, both run in ONE
+ * persistent launch with a device-wide barrier between them; otherwise two
+ * launches on `stream`.  w4a16_mlp_one_launch() tells which.  The results
+ * are bit-identical either way.
+ *   workspace : at least w4a16_workspace_size_mlp(M, H, F) bytes (never 0 for
+ *               a supported shape), 256-byte aligned.  Its first
+ *               W4A16_MLP_H_OFFSET bytes hold counters and barrier words:
+ *               they must be ZERO BEFORE THE FIRST CALL and every call leaves
+ *               them zero, except the barrier's generation word (the int at
+ *               W4A16_MLP_GENERATION_OFFSET), which may hold any value and
+ *               changes with every one-launch call.  h is left at byte
+ *               offset W4A16_MLP_H_OFFSET
+ *               (bf16 [M][F]).  The int at byte offset
+ *               W4A16_MLP_TIMEOUT_OFFSET becomes 1 if a workgroup of the
+ *               one-launch kernel stopped waiting at the barrier after its
+ *               poll limit (the grid was not all resident, e.g. another
+ *               process held the device): y of that call is then undefined;
+ *               the flag stays set until the caller clears it.  Calls that
+ *               share a workspace must not overlap in time.
+ */
+#define W4A16_MLP_H_OFFSET 10240
+#define W4A16_MLP_GENERATION_OFFSET 9344
+#define W4A16_MLP_TIMEOUT_OFFSET 9472
+w4a16_status_t w4a16_mlp_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,
+                                const float* g_gate, const uint8_t* wq_up, const uint8_t* ws_up,
+                                const float* g_up, const uint8_t* wq_down, const uint8_t* ws_down,
+                                const float* g_down, const uint16_t* x, uint16_t* y, int M, int H,
+                                int F, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/* Bytes of workspace w4a16_mlp_swiglu needs (0 = unsupported shape). */
+size_t w4a16_workspace_size_mlp(int M, int H, int F);
+
+/* 1 if w4a16_mlp_swiglu runs this shape in one launch on the current device,
+ * 0 if in two, -1 if the shape is unsupported. */
+int w4a16_mlp_one_launch(int M, int H, int F);
+
+/* Diagnostics and tests (process-wide, not thread-safe): mode 0 = one launch
+ * when possible (default), 1 = always two launches; spin_limit = barrier
+ * polls before a workgroup gives up waiting (default 2^20; 0 makes every
+ * workgroup but the last to arrive give up at once).  Returns 1, or 0 for
+ * an invalid argument (nothing changed). */
+int w4a16_mlp_set_options(int mode, int spin_limit);
+
 /* Bytes of workspace w4a16_quantize[_bf16] needs (0 = unsupported shape). */
 size_t w4a16_quantize_workspace_size(int N, int K);
 
@@ -176,7 +230,7 @@ size_t w4a16_workspace_size_gate_up(int M, int N, int K);
 const char* w4a16_status_string(w4a16_status_t status);
 
 /* ABI version of this header: bumped on any incompatible change. */
-#define W4A16_ABI_VERSION 2
+#define W4A16_ABI_VERSION 3
 int w4a16_abi_version(void);
 
 #ifdef __cplusplus

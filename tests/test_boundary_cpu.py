@@ -32,7 +32,9 @@ def lib():
 def test_header_declares_the_abi():
     names = declared_functions()
     for n in ("w4a16_gemm", "w4a16_gemm_gate_up_swiglu", "w4a16_dequant", "w4a16_workspace_size",
-              "w4a16_workspace_size_gate_up", "w4a16_status_string", "w4a16_abi_version"):
+              "w4a16_workspace_size_gate_up", "w4a16_status_string", "w4a16_abi_version",
+              "w4a16_mlp_swiglu", "w4a16_workspace_size_mlp", "w4a16_mlp_one_launch",
+              "w4a16_mlp_set_options"):
         assert n in names
 
 
@@ -43,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.w4a16_abi_version() == 2
+    assert lib.w4a16_abi_version() == 3
     for st in (0, 1, 2, 3):
         assert len(w4.status_string(st)) > 0
     assert w4.status_string(99) == "unknown status"
@@ -161,3 +163,53 @@ def test_argmax_argument_checks(lib):
     assert w4.workspace_size_argmax(12, 1000, 5120) > 0
     assert w4.workspace_size_argmax(1, 248320, 5120) >= 4096 + 8
     assert w4.workspace_size_argmax(16, 64, 17408) == 0        # would need a K split
+
+
+# ---- MLP block -----------------------------------------------------------------
+
+def call_mlp(lib, ptrs=None, M=1, H=256, F=512, work=P, wbytes=1 << 30):
+    p = dict(wq_g=P, ws_g=P, g_g=P, wq_u=P, ws_u=P, g_u=P, wq_d=P, ws_d=P, g_d=P, x=P, y=P)
+    p.update(ptrs or {})
+    return lib.w4a16_mlp_swiglu(*p.values(), M, H, F, work, wbytes, None)
+
+
+def test_mlp_argument_checks(lib):
+    for arg in ("wq_g", "ws_g", "g_g", "wq_u", "ws_u", "g_u", "wq_d", "ws_d", "g_d", "x", "y"):
+        assert call_mlp(lib, {arg: 0}) == w4.ERR_INVALID_VALUE, arg
+    assert call_mlp(lib, M=0) == w4.ERR_INVALID_VALUE
+    assert call_mlp(lib, M=33) == w4.ERR_UNSUPPORTED
+    assert call_mlp(lib, H=272) == w4.ERR_UNSUPPORTED
+    assert call_mlp(lib, F=400) == w4.ERR_UNSUPPORTED
+    for arg, off in (("wq_g", 8), ("ws_u", 4), ("wq_d", 8), ("x", 2), ("g_d", 2), ("y", 2)):
+        assert call_mlp(lib, {arg: P + off}) == w4.ERR_UNSUPPORTED, arg
+    need = w4.workspace_size_mlp(1, 256, 512)
+    assert call_mlp(lib, work=0, wbytes=need) == w4.ERR_INVALID_VALUE        # h lives there
+    assert call_mlp(lib, wbytes=need - 1) == w4.ERR_INVALID_VALUE
+    assert call_mlp(lib, work=P + 16, wbytes=need) == w4.ERR_UNSUPPORTED     # 256-byte alignment
+
+
+def test_mlp_workspace_layout(lib):
+    # no K split in either phase: counters and barrier words, then h (bf16 [M][F])
+    assert w4.workspace_size_mlp(1, 5120, 17408) == w4.MLP_H_OFFSET + 17408 * 2
+    assert w4.workspace_size_mlp(3, 256, 512) == w4.MLP_H_OFFSET + 3 * 512 * 2
+    # M = 7: the down projection splits K=17408; its fp32 partials follow h
+    size = w4.workspace_size_mlp(7, 5120, 17408)
+    down = w4.workspace_size(7, 5120, 17408) - 4096
+    assert size == w4.MLP_H_OFFSET + ((7 * 17408 * 2 + 255) // 256) * 256 + down
+    assert w4.workspace_size_mlp(33, 256, 512) == 0
+    assert w4.workspace_size_mlp(1, 272, 512) == 0
+    assert w4.MLP_H_OFFSET % 256 == 0
+    assert 8192 <= w4.MLP_GENERATION_OFFSET < w4.MLP_TIMEOUT_OFFSET < w4.MLP_H_OFFSET
+    hdr = open(HEADER).read()
+    for name in ("H_OFFSET", "GENERATION_OFFSET", "TIMEOUT_OFFSET"):
+        assert re.search(rf"#define W4A16_MLP_{name} {getattr(w4, 'MLP_' + name)}\b", hdr), name
+    assert lib.w4a16_mlp_one_launch(33, 256, 512) == -1
+
+
+def test_mlp_options(lib):
+    assert lib.w4a16_mlp_set_options(2, 10) == 0
+    assert lib.w4a16_mlp_set_options(0, -1) == 0
+    assert lib.w4a16_mlp_set_options(1, 5) == 1
+    assert lib.w4a16_mlp_set_options(0, 1 << 20) == 1
+    with pytest.raises(ValueError):
+        w4.mlp_set_options(3)

@@ -1,0 +1,199 @@
+"""GPU parity of the MLP block entry point (w4a16_mlp_swiglu) against the
+oracle: h = bf16(silu(x Wg^T) * (x Wu^T)), y = bf16(h Wd^T).  Checks every
+output against oracle.mlp_bound, the one-launch and two-launch paths against
+each other bit for bit, h against the gate/up entry point bit for bit, the
+barrier's time-out path (forced from the host with a poll limit of 0, so every
+kernel still runs to its end), workspace reuse across shapes and HIP-graph
+replays."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp4_w4a16_amd as w4
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = min(16, os.cpu_count() or 1)
+_CACHE = {}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w4.lib()
+    w4.mlp_set_options(0, 1 << 20)
+    yield
+    w4.mlp_set_options(0, 1 << 20)
+
+
+def d_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+
+
+def d_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).cuda().view(
+        torch.bfloat16)
+
+
+def d_g(g):
+    return torch.tensor([float(np.float32(g))], dtype=torch.float32, device="cuda")
+
+
+def h_f64(t):
+    bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return synth.bf16_to_f32(bits).astype(np.float64)
+
+
+def block(seed, M, H, F):
+    """Host weights (gate, up: [F][H]; down: [H][F]), x bits, and device copies."""
+    key = (seed, H, F)
+    if key not in _CACHE:
+        _CACHE[key] = tuple(synth.nvfp4_weights(seed + i, n, k)
+                            for i, (n, k) in enumerate(((F, H), (F, H), (H, F))))
+    host = _CACHE[key]
+    dev = tuple((d_u8(wq), d_u8(ws), d_g(g)) for wq, ws, g in host)
+    x = synth.activations(seed + 7, M, H)
+    return host, dev, x
+
+
+def h_of(work, M, F):
+    """h (bf16 [M][F]) from the MLP workspace, as int16 bit patterns."""
+    return work[w4.MLP_H_OFFSET:w4.MLP_H_OFFSET + M * F * 2].view(torch.int16).view(M, F).clone()
+
+
+def counters_zero(work):
+    """The workspace's counter and barrier words are all zero again (the
+    barrier's generation word may hold any value)."""
+    head = work[:w4.MLP_H_OFFSET].clone()
+    head[w4.MLP_GENERATION_OFFSET:w4.MLP_GENERATION_OFFSET + 4] = 0
+    return int(head.count_nonzero()) == 0
+
+
+def check(y, host, x, M, H, F, ctx):
+    out = oracle.mlp_swiglu(*host, x, M, H, F, nthreads=NTHREADS)
+    wd = np.abs(oracle.dequant_f64(*host[2], H, F))
+    bound = oracle.mlp_bound(out, wd)
+    got = h_f64(y)
+    err = np.abs(got - out["y"])
+    ratio = float(np.max(err / bound))
+    say(f"  {ctx}: max |err|/bound = {ratio:.3e}")
+    bad = ~(err <= bound)
+    if bad.any():
+        i = tuple(np.argwhere(bad)[0])
+        raise AssertionError(f"{ctx}: {int(bad.sum())} outputs outside the bound; first at {i}: "
+                             f"gpu {got[i]!r} ref {out['y'][i]!r} bound {bound[i]!r}")
+
+
+def run(dev, x_bits, M, H, F, mode, work=None):
+    w4.mlp_set_options(mode, 1 << 20)
+    try:
+        dx = d_bf16(x_bits)
+        if work is None:
+            work = w4.new_workspace_mlp(M, H, F, "cuda")
+        y = w4.mlp_swiglu(*dev, dx, workspace=work)
+        torch.cuda.synchronize()
+    finally:
+        w4.mlp_set_options(0, 1 << 20)
+    return y, work
+
+
+SHAPES = [(1, 512, 1024), (2, 256, 768), (3, 512, 512), (4, 512, 1024), (5, 256, 1280),
+          (7, 768, 1536), (8, 256, 4096), (13, 512, 768), (16, 512, 1024), (17, 256, 512),
+          (32, 256, 512)]
+
+
+@pytest.mark.parametrize("M,H,F", SHAPES)
+def test_mlp_matches_oracle_both_paths(M, H, F):
+    say(f"[mlp] M={M} H={H} F={F} one_launch={w4.mlp_one_launch(M, H, F)}")
+    host, dev, x = block(100 + M, M, H, F)
+    y1, work1 = run(dev, x, M, H, F, mode=0)
+    y2, work2 = run(dev, x, M, H, F, mode=1)
+    check(y1, host, x, M, H, F, f"M={M} H={H} F={F}")
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "one launch != two launches"
+    h1, h2 = h_of(work1, M, F), h_of(work2, M, F)
+    assert torch.equal(h1, h2)
+    ref_h = w4.gemm_gate_up_swiglu(*dev[0], *dev[1], d_bf16(x))
+    assert torch.equal(h1, ref_h.view(torch.int16)), "h differs from the gate/up entry point"
+    # counters and barrier words are left zero
+    assert counters_zero(work1) and counters_zero(work2)
+
+
+@pytest.mark.parametrize("M", [1, 7])
+def test_mlp_full_size(M):
+    H, F = 5120, 17408
+    assert w4.mlp_one_launch(M, H, F) == 1, "the benchmark shape should run in one launch"
+    say(f"[mlp full] M={M}")
+    host, dev, x = block(300, M, H, F)
+    y, work = run(dev, x, M, H, F, mode=0)
+    check(y, host, x, M, H, F, f"full M={M}")
+    y2, _ = run(dev, x, M, H, F, mode=1)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    assert counters_zero(work)
+
+
+def test_barrier_timeout_is_flagged_and_recovers():
+    M, H, F = 4, 512, 1024
+    assert w4.mlp_one_launch(M, H, F) == 1
+    host, dev, x = block(400, M, H, F)
+    dx = d_bf16(x)
+    work = w4.new_workspace_mlp(M, H, F, "cuda")
+    say("[mlp timeout] poll limit 0")
+    w4.mlp_set_options(0, 0)          # every workgroup but the last to arrive gives up at once
+    try:
+        w4.mlp_swiglu(*dev, dx, workspace=work)
+        torch.cuda.synchronize()
+    finally:
+        w4.mlp_set_options(0, 1 << 20)
+    flag = work[w4.MLP_TIMEOUT_OFFSET:w4.MLP_TIMEOUT_OFFSET + 4].view(torch.int32).item()
+    assert flag == 1
+    work[w4.MLP_TIMEOUT_OFFSET:w4.MLP_TIMEOUT_OFFSET + 4] = 0
+    assert counters_zero(work), "counters must be reset even after a time-out"
+    y = w4.mlp_swiglu(*dev, dx, workspace=work)
+    torch.cuda.synchronize()
+    check(y, host, x, M, H, F, "after time-out")
+    assert work[w4.MLP_TIMEOUT_OFFSET:w4.MLP_TIMEOUT_OFFSET + 4].view(torch.int32).item() == 0
+
+
+def test_workspace_reused_across_shapes():
+    H, F = 512, 4096
+    work = w4.new_workspace_mlp(8, H, F, "cuda")     # the largest of the calls below
+    for M in (8, 1, 3, 8, 5):
+        host, dev, x = block(500, M, H, F)
+        y, _ = run(dev, x, M, H, F, mode=0, work=work)
+        check(y, host, x, M, H, F, f"reuse M={M}")
+        assert counters_zero(work)
+
+
+def test_graph_capture_replays_match_eager():
+    for M, H, F in [(1, 5120, 17408), (7, 5120, 17408)]:
+        host, dev, x = block(600, M, H, F)
+        dx = d_bf16(x)
+        work = w4.new_workspace_mlp(M, H, F, "cuda")
+        eager = w4.mlp_swiglu(*dev, dx, workspace=work).clone()
+        y = torch.empty_like(eager)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            w4.mlp_swiglu(*dev, dx, y=y, workspace=work)
+        torch.cuda.current_stream().wait_stream(s)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            w4.mlp_swiglu(*dev, dx, y=y, workspace=work)
+        for _ in range(3):
+            y.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            _ = (dx.float() * 2).sum().item()
+            assert torch.equal(y.view(torch.int16), eager.view(torch.int16)), M
+        assert counters_zero(work)
