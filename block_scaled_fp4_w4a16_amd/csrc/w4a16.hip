@@ -154,12 +154,14 @@ Plan plan_gemm(int M, int N, int K, int epi) {
   // Launch rules from measured sweeps on MI355X over the benchmark shapes:
   // shallow rings (4 chunk loads in flight per lane); one workgroup of 8
   // waves per CU (x is staged into LDS once per workgroup, so fewer row
-  // blocks means less x traffic); VALU rows read by 16 lanes; MFMA tasks of
-  // one row quad (finer stream-K tasks beat two quads sharing x reads).
+  // blocks means less x traffic); VALU rows read by 32 lanes where K/32 is a
+  // multiple of 32 (512 contiguous bytes per row per load beat 256); MFMA
+  // tasks of one row quad (finer stream-K tasks beat two quads sharing x
+  // reads).
   pl.D = 4;
   int wmax, wg_per_cu;
   if (!pl.mfma) {
-    pl.lr = (CR % 16 == 0) ? 16 : 8;
+    pl.lr = (CR % 32 == 0) ? 32 : (CR % 16 == 0) ? 16 : 8;
     pl.LB = 1024;
     wmax = 8;
     wg_per_cu = 1;
@@ -352,9 +354,10 @@ struct MlpKernEntry {
 #define W4A16_MLPV(MT, L1, L2) \
   {false, MT, L1, L2, 4, 1024, reinterpret_cast<const void*>(&k_mlp_valu<MT, L1, L2, 4, 1024>)},
 #define W4A16_MLPV_L(L1, L2) W4A16_MLPV(1, L1, L2) W4A16_MLPV(2, L1, L2) W4A16_MLPV(3, L1, L2)
+#define W4A16_MLPV_L2(L1) W4A16_MLPV_L(L1, 32) W4A16_MLPV_L(L1, 16) W4A16_MLPV_L(L1, 8)
 #define W4A16_MLPM(P) {true, P, 1, 1, 4, 512, reinterpret_cast<const void*>(&k_mlp_mfma<P, 4, 512>)},
 const MlpKernEntry kMlpKernels[] = {
-    W4A16_MLPV_L(16, 16) W4A16_MLPV_L(16, 8) W4A16_MLPV_L(8, 16) W4A16_MLPV_L(8, 8)
+    W4A16_MLPV_L2(32) W4A16_MLPV_L2(16) W4A16_MLPV_L2(8)
     W4A16_MLPM(1) W4A16_MLPM(2) W4A16_MLPM(3) W4A16_MLPM(4)
     W4A16_MLPM(5) W4A16_MLPM(6) W4A16_MLPM(7) W4A16_MLPM(8)};
 
