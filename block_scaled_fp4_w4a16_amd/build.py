@@ -28,6 +28,9 @@ def build_command(out: str, extra=()) -> list:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
         # no packed-fp32 VALU instructions (v_pk_fma_f32 and friends)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # one-lane atomics stay plain: the optimizer's lane combining would wait
+        # for the batch counter's result right after issuing it
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
         *extra, "-o", out, SRC,
     ]

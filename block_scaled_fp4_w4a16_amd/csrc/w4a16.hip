@@ -200,6 +200,9 @@ Plan plan_gemm(int M, int N, int K, int epi) {
       pl.mfma ? (size_t)pl.lr * ((M + 3) / 4) * 4 * 16
               : (size_t)(64 / pl.lr) * M * (pl.lr < 16 ? 1 : pl.lr / 16);
   const size_t seg_vals = pl.mfma ? (size_t)pl.lr * ((M + 3) / 4) * 16 : (size_t)(64 / pl.lr) * M;
+  // VALU step partial: (64 / L) row slots x (L / 16 or 1) DPP groups x M
+  const size_t valu_step_vals =
+      pl.mfma ? 0 : (size_t)(64 / pl.lr) * (pl.lr > 16 ? pl.lr / 16 : 1) * M;
   const long long groups = ((long long)N + RT - 1) / RT;  // row groups in total
   // Smallest K split whose x slice, scratch and segment partials fit in LDS
   // (VALU: whole chunk steps per lane) with one row block per CU and split.
@@ -230,12 +233,18 @@ Plan plan_gemm(int M, int N, int K, int epi) {
     // LDS bytes for W waves: x slice, per-wave scratch, segment slots and
     // the task bookkeeping (two ints per segment slot, one per wave)
     auto lds_for = [&](int W, long long* kmax_out) {
+      const size_t xbytes = (size_t)xrows * (size_t)(CRS * 4 + 1) * 16;
+      if (!pl.mfma) {
+        // VALU: one partial per step (G row slots x DPP groups x M) and the
+        // batch counter
+        if (kmax_out) *kmax_out = 0;
+        return xbytes + (size_t)TS * (size_t)valu_step_vals * sizeof(float) + 16;
+      }
       const long long steps = (TS + W - 1) / W;  // most steps of one wave
       long long kmax = (steps - 1 + CPL - 1) / CPL + 1;
       if (kmax > ntasks) kmax = ntasks;
       if (kmax_out) *kmax_out = kmax;
-      return (size_t)xrows * (size_t)(CRS * 4 + 1) * 16 +
-             (scr_per_wave + (size_t)kmax * seg_vals) * sizeof(float) * W +
+      return xbytes + (scr_per_wave + (size_t)kmax * seg_vals) * sizeof(float) * W +
              (2 * (size_t)kmax + 1) * sizeof(int) * W;
     };
     // the split is chosen for the largest wave count (so that it does not

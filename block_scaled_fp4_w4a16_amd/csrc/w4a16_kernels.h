@@ -448,13 +448,26 @@ constexpr int kNoTask = 1 << 30;
 // lane (slot r, position p) reads chunk p + L*jj of row r of the task, so the
 // L lanes of a row read L*16 contiguous bytes per load.  A task is one row
 // group (G rows; for the fused variant G/2 gate rows plus the same G/2 up
-// rows) and takes CPL = CRS/L steps.  Each lane keeps D chunk loads in
-// flight in a register ring that runs across task boundaries.
+// rows) and takes CPL = CRS/L steps; the workgroup has TS = ntasks*CPL steps,
+// step s = task*CPL + jj.
 //
-// Per chunk and activation row: 16 bf16x2 dot products per 32 weights into
-// two block partials, then acc += partial * e4m3(scale).  x rows live in LDS
-// (swizzled) and are read with 128-bit LDS loads; lanes of different slots
-// read the same x (broadcast).
+// Scheduling: steps are handed out in batches of D consecutive steps.  Wave w
+// starts with batch w (steps wD .. wD+D-1, so its loads can be issued before
+// the x barrier); afterwards each wave takes the next batch from a workgroup
+// counter in LDS (one LDS atomic per batch), so a wave whose loads return
+// late takes fewer batches and the waves of a workgroup finish together.
+// Each lane keeps D chunk loads in flight in a register ring: slot d holds
+// step d of the current batch and is refilled with step d of the next batch
+// as soon as it has been consumed.
+//
+// Per step and activation row: 16 bf16x2 dot products per 32 weights into
+// two block partials, times their e4m3 scales; the L lanes of a row are
+// summed with DPP (groups of up to 16 lanes) and the group totals are parked
+// in LDS at part[step][slot][group][m].  After one barrier every output row
+// adds its task's step partials in step order and group order: a fixed
+// order, so results do not depend on which wave ran which step.  x rows live
+// in LDS (swizzled) and are read with 128-bit LDS loads; lanes of different
+// slots read the same x (broadcast).
 // ---------------------------------------------------------------------------
 template <int MT, int L, int D, int EPI, int LB, int CO>
 W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
@@ -466,7 +479,7 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
   constexpr int RT = FUSED ? G / 2 : G;   // output rows per task
   constexpr int GL = L < 16 ? L : 16;     // lanes summed by DPP
   constexpr int NSEG = L / GL;            // DPP groups per row slot
-  constexpr int V = G * MT;               // values in a segment partial: [slot][m]
+  constexpr int V = G * NSEG * MT;        // values in a step partial: [slot][group][m]
   const int W = blockDim.x >> 6, NT = blockDim.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -476,74 +489,61 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
   const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
   const int row_hi = row_lo + a.rq + (rb < a.rr ? 1 : 0);
   const int ntasks = (row_hi - row_lo + RT - 1) / RT;
-  const StreamSplit split{ntasks * CPL, W, a.rW};
-  const int s_begin = split.begin(wv);
-  const int T = split.begin(wv + 1) - s_begin;  // steps of this wave (uniform)
-  const int ft = div_small(s_begin, CPL, a.rCPL), jj0 = s_begin - ft * CPL;  // first task, its first step
+  const int TS = ntasks * CPL;
   const int p = lane % L, r = lane / L;
   const int srow = FUSED ? (r % (G / 2)) : r;
   const bool is_up = FUSED && (r >= G / 2);
   const uint8_t* wq = is_up ? a.wq1 : a.wq0;
   const uint8_t* ws = is_up ? a.ws1 : a.ws0;
-  float* scr = reinterpret_cast<float*>(xs + MT * RSU) + wv * (G * MT * NSEG);
-  float* seg = reinterpret_cast<float*>(xs + MT * RSU) + W * (G * MT * NSEG);
-  int* tw0 = reinterpret_cast<int*>(seg + W * a.kmax * V);
-  int* tw1 = tw0 + W * a.kmax;
-  int* wft = tw1 + W * a.kmax;
+  float* part = reinterpret_cast<float*>(xs + MT * RSU);  // [TS][V]
+  int* next_batch = reinterpret_cast<int*>(part + (size_t)TS * V);
 
-  // ---- issue cursor: (task it_i, step jj_i) -> row pointers -------------
+  // ---- issue cursor: step (task it_i, jj_i) -> row pointers ---------------
   const uint4* qp;
   const uint16_t* sp;
-  int s_i = 0, it_i = ft, jj_i = jj0;
+  int it_i, jj_i;
   auto set_task = [&](int it) {
     int row = row_lo + it * RT + srow;
     row = row < row_hi ? row : row_hi - 1;
     qp = reinterpret_cast<const uint4*>(wq + (size_t)row * (size_t)(K >> 1)) + c0 + p;
     sp = reinterpret_cast<const uint16_t*>(ws + (size_t)row * (size_t)(K >> 4)) + c0 + p;
   };
-  set_task(it_i);
+  // position the cursor at step s (steps past the end load the last step;
+  // their data is never used)
+  auto seek = [&](int s) {
+    s = s < TS ? s : TS - 1;
+    it_i = div_small(s, CPL, a.rCPL);
+    jj_i = s - it_i * CPL;
+    set_task(it_i);
+  };
   uint4 qb[D];
   uint32_t sb[D];
-  // load the current cursor position into slot d, then advance (the cursor
-  // stops at the last step; later loads repeat it and are never used)
+  // load the cursor's step into slot d, then advance (stopping at the last step)
   auto issue = [&](int d) {
     qb[d] = load_stream(qp + L * jj_i);
     sb[d] = __builtin_nontemporal_load(sp + L * jj_i);
-    if (s_i + 1 < T) {
-      ++s_i;
-      if (++jj_i == CPL) {
-        jj_i = 0;
-        ++it_i;
-        set_task(it_i);
-      }
+    if (it_i * CPL + jj_i + 1 < TS && ++jj_i == CPL) {
+      jj_i = 0;
+      ++it_i;
+      set_task(it_i);
     }
   };
-  // x -> LDS (rows of K bf16 in 16-byte units, swizzled): ring slot 0, the
-  // x loads, the rest of the weight prologue, then the LDS stores (loads
-  // complete in order, so the stores wait for slot 0 and x only)
+  // x -> LDS (rows of K bf16 in 16-byte units, swizzled): ring slot 0 of the
+  // first batch, the x loads, the rest of the first batch, then the LDS
+  // stores (loads complete in order, so the stores wait for slot 0 and x only)
   constexpr int XMAX = LB > 512 ? 8 : 16;
   uint4 xr[XMAX];
   auto xpos = [](int cu) { return xsw(cu >> 2, cu & 3); };
-#ifndef W4A16_WEIGHTS_FIRST
-  // ring slot 0 first: the weight stream starts as early in the (cold)
-  // instruction stream as possible, and the first step needs it anyway
+  int base = wv * D;  // first step of this wave's current batch
+  seek(base);
   issue(0);
   x_stage_issue<XC>(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
 #pragma unroll
   for (int d = 1; d < D; ++d) issue(d);
-#else
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue(d);
-#endif
-  // (issue is unconditional: a wave without steps loads its clamped start
-  // position)
   W4A16_STAMP(t_issued);
   const float gv0 = load_f32_vmem(a.g0);
   const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
-  if (lane == 0) wft[wv] = T > 0 ? ft : kNoTask;
-#ifdef W4A16_WEIGHTS_FIRST
-  x_stage_issue<XC>(xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, tid, NT);
-#endif
+  if (tid == 0) *next_batch = W * D;
   x_stage_store<XC>(xs, xr, a.x, a.M, MT, K, c0 << 2, CRS << 2, a.rUPR, RSU, tid, NT, xpos);
   __syncthreads();
   W4A16_STAMP(t_barrier);
@@ -551,43 +551,25 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
   unsigned long long t_first = 0;
 #endif
 
-  float acc[MT];
+  while (base < TS) {
+    // the next batch: one LDS atomic by lane 0, broadcast to the wave
+    int nxt_lane0 = 0;  // read back only after the first step (see below)
+    if (lane == 0)
+      nxt_lane0 = __hip_atomic_fetch_add(next_batch, D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    int nxt = 0;
+    // compute cursor of the current batch; a run is the batch's steps of one
+    // task: its sum stays in registers and is reduced and parked once, in
+    // the slot of its first step
+    int jj_c = base - div_small(base, CPL, a.rCPL) * CPL;
+    int run0 = base;
+    float acc[MT];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-  int jj_c = jj0, kseg = 0;
-
-  // Segment end: sum each row slot's L lanes (DPP inside groups of up to 16
-  // lanes, then the NSEG group totals through the per-wave LDS scratch) and
-  // park the slot totals [slot][m] in segment slot (wv, kseg).
-  auto finish_segment = [&](bool task_end) {
-    const int sg = p / GL;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float v = group_allreduce<GL>(acc[m]);
-      if ((p % GL) == 0) scr[(r * MT + m) * NSEG + sg] = v;
-      acc[m] = 0.0f;
-    }
-    wave_lds_sync();
-    if (lane < V) {
-      float v = 0.0f;
-#pragma unroll
-      for (int i = 0; i < NSEG; ++i) v += scr[lane * NSEG + i];
-      seg[(wv * a.kmax + kseg) * V + lane] = v;
-    }
-    if (lane == 0) {
-      if (kseg > 0 || jj0 == 0) tw0[ft + kseg] = wv;
-      if (task_end) tw1[ft + kseg] = wv;
-    }
-    ++kseg;
-    wave_lds_sync();
-  };
-
-  for (int s0 = 0; s0 < T; s0 += D) {
+    for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      // consume slot d completely, then refill it (the refill can then reuse
-      // the slot's registers: no copies and no full drain at the loop edge)
-      if (s0 + d < T) {
+      // consume slot d completely, then refill it with step d of the next batch
+      const int s = base + d;
+      if (s < TS) {
         const uint4 q = qb[d];
         const uint32_t sc = sb[d];
         const int c = p + L * jj_c;
@@ -629,27 +611,55 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
         W4A16_DOT_WORD(q.w, 3, bhi)
 #undef W4A16_DOT_WORD
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          acc[m] = fmaf(blo[m], s_lo, acc[m]);
-          acc[m] = fmaf(bhi[m], s_hi, acc[m]);
-        }
+        for (int m = 0; m < MT; ++m) acc[m] = fmaf(blo[m], s_lo, fmaf(bhi[m], s_hi, acc[m]));
 #ifdef W4A16_TRACE
         if (t_first == 0) t_first = wall_clock64();
 #endif
         const bool task_end = ++jj_c == CPL;
-        if (task_end || s0 + d + 1 == T) finish_segment(task_end);
+        if (task_end || d == D - 1 || s + 1 == TS) {
+          float* ps = part + (size_t)run0 * V + (r * NSEG + p / GL) * MT;
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            const float v = group_allreduce<GL>(acc[m]);
+            if ((p % GL) == 0) ps[m] = v;
+            acc[m] = 0.0f;
+          }
+          run0 = s + 1;
+        }
         if (task_end) jj_c = 0;
+      }
+      // the issue cursor moves to the next batch only here, so that the
+      // batch counter's latency hides behind the first step's work
+      if (d == 0) {
+        nxt = __builtin_amdgcn_readfirstlane(nxt_lane0);
+        seek(nxt);
       }
       issue(d);
     }
+    base = nxt;
   }
   W4A16_STAMP(t_end);
 
-  // ---- workgroup combine: output (row n, m) = sum of its task's segments --
+  // ---- workgroup combine: output (row n, m) = its task's step partials ----
   __syncthreads();
   const float ig0 = 1.0f / gv0;
   const float ig1 = FUSED ? 1.0f / gv1 : 1.0f;
   const int nrows = row_hi - row_lo;
+  // sum of slot `slot`'s values for activation row m over the task's runs
+  // (a run starts at the task's first step and at every batch start), in
+  // step order
+  auto row_sum = [&](int t, int slot, int m) {
+    float v = 0.0f;
+    const int s0 = t * CPL;
+    const float* pt = part + slot * NSEG * MT + m;
+    int s = s0;
+    while (s < s0 + CPL) {
+#pragma unroll
+      for (int g = 0; g < NSEG; ++g) v += pt[(size_t)s * V + g * MT];
+      s = (s / D + 1) * D;  // the next batch start (D is a power of two here)
+    }
+    return v;
+  };
   if (EPI == kEpiArgmax) {
     // S == 1 here (the host rejects a K split with this epilogue); x is no
     // longer needed, so its LDS holds the reduction scratch
@@ -660,12 +670,7 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
       int bi = kNoIndex;
       for (int n = tid; n < nrows; n += NT) {
         const int t = n / RT, rt = n - t * RT;
-        float v = 0.0f;
-        for (int w = tw0[t]; w <= tw1[t]; ++w) {
-          const int k = t - wft[w];
-          if (k >= 0) v += seg[(w * a.kmax + k) * V + rt * MT + m];
-        }
-        argmax_take(bv, bi, v * ig0, row_lo + n);
+        argmax_take(bv, bi, row_sum(t, rt, m) * ig0, row_lo + n);
       }
       wg_argmax(bv, bi, red, W);
       if (tid == 0) {
@@ -678,30 +683,18 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
   } else
   for (int n = tid; n < nrows; n += NT) {
     const int t = n / RT, rt = n - t * RT;
-    const int w0 = tw0[t], w1 = tw1[t];
-    float v[MT], u[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) v[m] = u[m] = 0.0f;
-    for (int w = w0; w <= w1; ++w) {
-      const int k = t - wft[w];
-      if (k < 0) continue;  // a wave without steps
-      const float* sg = seg + (w * a.kmax + k) * V;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        v[m] += sg[rt * MT + m];
-        if (FUSED) u[m] += sg[(rt + G / 2) * MT + m];
-      }
-    }
     const int row = row_lo + n;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
+      const float v = row_sum(t, rt, m);
+      const float u = FUSED ? row_sum(t, rt + G / 2, m) : 0.0f;
       if (S > 1) {
-        store_coherent(a.part + ((size_t)ks * a.M + m) * a.N + row, v[m]);
-        if (FUSED) store_coherent(a.part + ((size_t)(S + ks) * a.M + m) * a.N + row, u[m]);
+        store_coherent(a.part + ((size_t)ks * a.M + m) * a.N + row, v);
+        if (FUSED) store_coherent(a.part + ((size_t)(S + ks) * a.M + m) * a.N + row, u);
       } else if (FUSED) {
-        store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(silu(v[m] * ig0) * (u[m] * ig1)));
+        store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(silu(v * ig0) * (u * ig1)));
       } else {
-        store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(v[m] * ig0));
+        store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(v * ig0));
       }
     }
   }
