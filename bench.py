@@ -167,7 +167,7 @@ def bench_square(args, dev, stream):
 
 def graph_time(fns, cycles, stream):
     """Seconds per call of fns, captured once in a HIP graph (one call each)
-    and replayed `cycles` times after one untimed replay."""
+    and replayed `cycles` times after at least 50 ms of untimed replays."""
     import torch
     cap = torch.cuda.Stream()
     cap.wait_stream(stream)
@@ -181,9 +181,15 @@ def graph_time(fns, cycles, stream):
         for f in fns:
             f(cap)
     torch.cuda.synchronize()
-    with torch.cuda.stream(stream):
-        graph.replay()
-    torch.cuda.synchronize()
+    # untimed replays for at least 50 ms, so that the first configuration timed
+    # after the host-side weight generation runs at steady clocks
+    t_warm = time.perf_counter()
+    while True:
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_warm >= 0.05:
+            break
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
