@@ -42,9 +42,17 @@ constexpr size_t kMaxLds = 160 * 1024 - 256;
 constexpr size_t kCounterBytes = 4096;
 constexpr int kMaxSplitRowBlocks = (int)(kCounterBytes / sizeof(int));
 
+// Activation rows up to which the VALU kernel runs; the MFMA kernel takes
+// the rest.  Its cost is flat up to four rows while the VALU kernel's grows
+// with every row: measured by HIP-graph replay on MI355X, M = 3 ran 8-20 %
+// faster on the MFMA kernel (square 5120^2 7.07 vs 7.72 us, down 17408 ->
+// 5120 14.1 vs 17.6 us, gate/up 2 x 17408 x 5120 22.3 vs 27.0 us); M = 2 was
+// mixed (VALU faster on the square and gate/up shapes) and M = 1 is VALU's.
+constexpr int kValuMaxM = 2;
+
 // How one matmul call is launched.
 struct Plan {
-  bool mfma;   // false: VALU kernel (M <= 3); true: 4x4x4 MFMA kernel
+  bool mfma;   // false: VALU kernel (M <= kValuMaxM); true: 4x4x4 MFMA kernel
   int lr;      // VALU: lanes per weight row L; MFMA: row quads per task R
   int D;       // chunk loads in flight per lane (ring depth)
   int W;       // waves per workgroup
@@ -73,7 +81,7 @@ struct KernEntry {
   {false, MT, L, D, F, LB, reinterpret_cast<const void*>(&k_gemm_valu<MT, L, D, F, LB>)},
 #define W4A16_ME(P, R, D, F, LB) \
   {true, P, R, D, F, LB, reinterpret_cast<const void*>(&k_gemm_mfma<P, R, D, F, LB>)},
-#define W4A16_VALU_ALL_MT(L, D, F, LB) W4A16_VE(1, L, D, F, LB) W4A16_VE(2, L, D, F, LB) W4A16_VE(3, L, D, F, LB)
+#define W4A16_VALU_ALL_MT(L, D, F, LB) W4A16_VE(1, L, D, F, LB) W4A16_VE(2, L, D, F, LB)
 #define W4A16_MFMA_ALL_P(R, D, F, LB) \
   W4A16_ME(1, R, D, F, LB) W4A16_ME(2, R, D, F, LB) W4A16_ME(3, R, D, F, LB) W4A16_ME(4, R, D, F, LB)
 
@@ -150,7 +158,7 @@ Plan plan_gemm(int M, int N, int K, int epi) {
   Plan pl{};
   const int cus = cu_count();
   const int CR = K >> 5;  // 16-byte chunks per weight row (a multiple of 8)
-  pl.mfma = M > 3;
+  pl.mfma = M > kValuMaxM;
   // Launch rules from measured sweeps on MI355X over the benchmark shapes:
   // shallow rings (4 chunk loads in flight per lane); one workgroup of 8
   // waves per CU (x is staged into LDS once per workgroup, so fewer row
@@ -362,7 +370,7 @@ struct MlpKernEntry {
 };
 #define W4A16_MLPV(MT, L1, L2) \
   {false, MT, L1, L2, 4, 1024, reinterpret_cast<const void*>(&k_mlp_valu<MT, L1, L2, 4, 1024>)},
-#define W4A16_MLPV_L(L1, L2) W4A16_MLPV(1, L1, L2) W4A16_MLPV(2, L1, L2) W4A16_MLPV(3, L1, L2)
+#define W4A16_MLPV_L(L1, L2) W4A16_MLPV(1, L1, L2) W4A16_MLPV(2, L1, L2)
 #define W4A16_MLPV_L2(L1) W4A16_MLPV_L(L1, 32) W4A16_MLPV_L(L1, 16) W4A16_MLPV_L(L1, 8)
 #define W4A16_MLPM(P) {true, P, 1, 1, 4, 512, reinterpret_cast<const void*>(&k_mlp_mfma<P, 4, 512>)},
 const MlpKernEntry kMlpKernels[] = {

@@ -219,6 +219,42 @@ W4A16_DEV void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Keeps v computed at this point (an empty asm that takes and returns it):
+// the compiler would otherwise sink 1/g to its uses after the main loop,
+// where consuming the g load means waiting for the ring's last refills.
+W4A16_DEV float pin(float v) {
+  __asm__ volatile("" : "+v"(v));
+  return v;
+}
+
+// Address read by the MFMA kernel's ring refills past a wave's last step
+// (they keep every slot's load count fixed, so each wait stays exact; nothing
+// reads their data): 16 bytes of the first row of x (K/8 units), unit `tid` modulo the
+// largest power of two that fits, so the workgroup spreads them over up to
+// 8 KiB of lines it has just staged and that are served from cache.  A phase
+// that reads x coherently (x is written by the same launch) reads the first
+// weight row (K/32 units) instead, which no launch writes.
+template <bool XC>
+W4A16_DEV const uint4* past_line(const MatArgs& a, int tid) {
+  const int units = XC ? a.K >> 5 : a.K >> 3;             // >= 8, a multiple of 8
+  const int mask = (1 << (31 - __builtin_clz(units))) - 1;  // largest power of two <= units, minus 1
+  const uint4* base = XC ? reinterpret_cast<const uint4*>(a.wq0) : reinterpret_cast<const uint4*>(a.x);
+  return base + (tid & mask);
+}
+
+// Workgroup barrier for data in LDS only: each wave waits for its own LDS
+// operations, not for its global loads.  After the MFMA kernel's main loop
+// its load ring still holds refills issued past the last step (past_line);
+// nothing reads them, so the combine does not wait for them.  (Measured on
+// the VALU kernel the same changes gained nothing: there the combine's cost
+// is its own cold code path, and a g load moved ahead of x delayed the
+// prologue, so that kernel keeps re-reading its last step.)
+W4A16_DEV void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Position of 16-byte unit q (0..3) of x-chunk c inside an LDS x row for the
 // VALU kernel.  Lanes read consecutive chunks; the XOR spreads the four units
 // of neighbouring chunks over distinct bank groups (for 8- and 16-lane passes).
@@ -442,7 +478,8 @@ struct StreamSplit {
 constexpr int kNoTask = 1 << 30;
 
 // ---------------------------------------------------------------------------
-// VALU kernel, M = MT in {1, 2, 3}.
+// VALU kernel, M = MT in {1, 2} (the launch rules send M >= 3 to the MFMA
+// kernel; the body itself takes any small MT).
 //
 // Lane layout: a wave holds G = 64/L row slots of L lanes; at step (task, jj)
 // lane (slot r, position p) reads chunk p + L*jj of row r of the task, so the
@@ -509,7 +546,8 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
     sp = reinterpret_cast<const uint16_t*>(ws + (size_t)row * (size_t)(K >> 4)) + c0 + p;
   };
   // position the cursor at step s (steps past the end load the last step;
-  // their data is never used)
+  // their data is never used, and they keep every slot's load count fixed so
+  // that each wait stays exact)
   auto seek = [&](int s) {
     s = s < TS ? s : TS - 1;
     it_i = div_small(s, CPL, a.rCPL);
@@ -712,7 +750,8 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel, 4 <= M <= 32 (P = ceil(M/4) passes of 4 activation rows).
+// MFMA kernel, 3 <= M <= 32 (P = ceil(M/4) passes of 4 activation rows; rows
+// M..4P-1 are zero).
 //
 // Uses v_mfma_f32_4x4x4_16b_bf16: 16 independent 4x4x4 products per
 // instruction; lane l = 4*beta + j holds B[k=0..3][col j] and A[row j][k] of
@@ -765,7 +804,13 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
 
   const uint4* qp[R];
   const uint16_t* sp[R];
-  int s_i = 0, it_i = ft, jj_i = jj0;
+  // s_i: index of the step the next issue loads (among this wave's T steps).
+  // Past the last one the ring is still refilled (every wait stays exact) with
+  // loads of a cached line (past_line); cb is then 0, so each lane reads its
+  // own 16 bytes there.
+  const uint4* const q_past = past_line<XC>(a, tid);
+  const uint16_t* const s_past = reinterpret_cast<const uint16_t*>(q_past);
+  int s_i = 0, it_i = ft, jj_i = jj0, cb = beta;
   auto set_task = [&](int it) {
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
@@ -776,16 +821,28 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
     }
   };
   set_task(it_i);
+  auto go_past = [&]() {
+    s_i = T;
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      qp[rr] = q_past;
+      sp[rr] = s_past;
+    }
+    cb = 0;
+    jj_i = 0;
+  };
+  if (T == 0) go_past();
   uint4 qb[D][R];
   uint32_t sb[D][R];
   auto issue = [&](int d) {
-    int c = beta + 16 * jj_i;
+    int c = cb + 16 * jj_i;
     c = c < CRS ? c : CRS - 1;
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
       qb[d][rr] = load_stream(qp[rr] + c);
       sb[d][rr] = __builtin_nontemporal_load(sp[rr] + c);
     }
+    if (s_i >= T) return;  // past the end: stay there
     if (s_i + 1 < T) {
       ++s_i;
       if (++jj_i == CPL) {
@@ -793,6 +850,8 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
         ++it_i;
         set_task(it_i);
       }
+    } else {
+      go_past();
     }
   };
   // x -> LDS: rows 0..4P-1 (rows >= M are zero), 16 B pad per row.
@@ -838,11 +897,14 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
     for (int d = 1; d < D; ++d) issue(d);
     x_stage_store<XC>(xs, xr, a.x, a.M, 4 * P, K, c0 << 2, upr, a.rUPR, RSU, tid, NT, xpos);
   }
-  // (issue is unconditional: a wave without steps loads its clamped start
-  // position)
+  // (issue is unconditional: a wave without steps loads its cached line)
   W4A16_STAMP(t_issued);
   __syncthreads();
   W4A16_STAMP(t_barrier);
+  // g was the first load: 1/g costs no wait here (after the loop it made the
+  // combine wait for every refill still in flight)
+  const float ig0 = pin(1.0f / gv0);
+  const float ig1 = FUSED ? pin(1.0f / gv1) : 1.0f;
 #ifdef W4A16_TRACE
   unsigned long long t_first = 0;
 #endif
@@ -950,9 +1012,7 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
   W4A16_STAMP(t_end);
 
   // ---- workgroup combine: output (row n, m) = sum of its task's segments --
-  __syncthreads();
-  const float ig0 = 1.0f / gv0;
-  const float ig1 = FUSED ? 1.0f / gv1 : 1.0f;
+  lds_barrier();
   const int M = a.M;
   const int nrows = row_hi - row_lo;
   if (EPI == kEpiArgmax) {

@@ -90,7 +90,7 @@ W4A16_DEV void phase_coords(int id, int nrb, int& rb, int& ks) {
   rb = id - ks * nrb;
 }
 
-// M <= 3: both phases on the VALU kernel body (L1, L2 lanes per weight row).
+// M <= 2: both phases on the VALU kernel body (L1, L2 lanes per weight row).
 template <int MT, int L1, int L2, int D, int LB>
 __global__ void __launch_bounds__(LB) k_mlp_valu(MlpArgs m) {
   const int id = blockIdx.x;
@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(LB) k_mlp_valu(MlpArgs m) {
   }
 }
 
-// 4 <= M <= 32: both phases on the MFMA kernel body (P passes of 4 rows).
+// 3 <= M <= 32: both phases on the MFMA kernel body (P passes of 4 rows).
 template <int P, int D, int LB>
 __global__ void __launch_bounds__(LB) k_mlp_mfma(MlpArgs m) {
   const int id = blockIdx.x;
