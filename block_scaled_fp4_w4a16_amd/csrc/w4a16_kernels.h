@@ -408,29 +408,49 @@ W4A16_DEV void argmax_take(float& bv, int& bi, float v, int i) {
     bi = i;
   }
 }
-// Workgroup-wide argmax of one (v, i) per thread; the result is valid in
-// thread 0.  red: LDS scratch of at least 2 words per wave.
-W4A16_DEV void wg_argmax(float& v, int& i, float* red, int W) {
+constexpr int kNoIndex = 0x7fffffff;
+
+// Workgroup-wide argmax of up to MB activation rows at once: every thread
+// brings one candidate (v[m], ix[m]) per row m; afterwards thread m (m < M)
+// holds row m's winner in v[0], ix[0].  The rows are reduced side by side
+// (their wave-level exchanges are independent), with one pass through LDS
+// for all of them.  red: LDS scratch of 2 * MB words per wave.
+template <int MB>
+W4A16_DEV void wg_argmax_rows(float (&v)[MB], int (&ix)[MB], int M, float* red, int W) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
-    const float ov = __shfl_xor(v, off);
-    const int oi = __shfl_xor(i, off);
-    argmax_take(v, i, ov, oi);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      const float ov = __shfl_xor(v[m], off);
+      const int oi = __shfl_xor(ix[m], off);
+      argmax_take(v[m], ix[m], ov, oi);
+    }
   }
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    red[2 * w] = v;
-    red[2 * w + 1] = __int_as_float(i);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      red[(w * MB + m) * 2] = v[m];
+      red[(w * MB + m) * 2 + 1] = __int_as_float(ix[m]);
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0)
-    for (int k = 1; k < W; ++k) argmax_take(v, i, red[2 * k], __float_as_int(red[2 * k + 1]));
-  __syncthreads();
+  const int t = threadIdx.x;
+  float bv = -__builtin_inff();
+  int bi = kNoIndex;
+  if (t < M)
+    for (int k = 0; k < W; ++k)
+      argmax_take(bv, bi, red[(k * MB + t) * 2], __float_as_int(red[(k * MB + t) * 2 + 1]));
+  __syncthreads();  // red is free again
+  v[0] = bv;
+  ix[0] = bi;
 }
-constexpr int kNoIndex = 0x7fffffff;
 
 // Called by every thread once the workgroup's candidates cand[rb][m] are
-// stored: the last workgroup reduces all of them into idx[m], val[m].
+// stored: the last workgroup reduces all of them into idx[m], val[m].  Each
+// thread issues the loads of all its candidates' rows before using any of
+// them (they come from beyond the XCD caches: one round trip, not one per row).
+template <int MB>
 W4A16_DEV void argmax_finish(const MatArgs& a, int nwg, float* red, int W) {
   __shared__ int is_last;
   __builtin_amdgcn_s_waitcnt(0);
@@ -442,18 +462,34 @@ W4A16_DEV void argmax_finish(const MatArgs& a, int nwg, float* red, int W) {
   }
   __syncthreads();
   if (!is_last) return;
-  for (int m = 0; m < a.M; ++m) {
-    float bv = -__builtin_inff();
-    int bi = kNoIndex;
-    for (int b = threadIdx.x; b < nwg; b += W * 64) {
-      const float* c = a.cand + ((size_t)b * a.M + m) * 2;
-      argmax_take(bv, bi, load_coherent(c), __float_as_int(load_coherent(c + 1)));
+  const int M = a.M;
+  float bv[MB];
+  int bi[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    bv[m] = -__builtin_inff();
+    bi[m] = kNoIndex;
+  }
+  for (int b = threadIdx.x; b < nwg; b += W * 64) {
+    const float* c = a.cand + (size_t)b * M * 2;
+    float cv[MB];
+    int ci[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      cv[m] = -__builtin_inff();
+      ci[m] = kNoIndex;
+      if (m < M) {
+        cv[m] = load_coherent(c + 2 * m);
+        ci[m] = __float_as_int(load_coherent(c + 2 * m + 1));
+      }
     }
-    wg_argmax(bv, bi, red, W);
-    if (threadIdx.x == 0) {
-      a.amax_idx[m] = bi == kNoIndex ? -1 : bi;
-      a.amax_val[m] = bv;
-    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) argmax_take(bv[m], bi[m], cv[m], ci[m]);
+  }
+  wg_argmax_rows<MB>(bv, bi, M, red, W);
+  if ((int)threadIdx.x < M) {
+    a.amax_idx[threadIdx.x] = bi[0] == kNoIndex ? -1 : bi[0];
+    a.amax_val[threadIdx.x] = bv[0];
   }
 }
 
@@ -702,22 +738,25 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
     // S == 1 here (the host rejects a K split with this epilogue); x is no
     // longer needed, so its LDS holds the reduction scratch
     float* red = reinterpret_cast<float*>(xs);
+    float bv[MT];
+    int bi[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      float bv = -__builtin_inff();
-      int bi = kNoIndex;
-      for (int n = tid; n < nrows; n += NT) {
-        const int t = n / RT, rt = n - t * RT;
-        argmax_take(bv, bi, row_sum(t, rt, m) * ig0, row_lo + n);
-      }
-      wg_argmax(bv, bi, red, W);
-      if (tid == 0) {
-        float* c = a.cand + ((size_t)rb * a.M + m) * 2;
-        store_coherent(c, bv);
-        store_coherent(c + 1, __int_as_float(bi));
-      }
+      bv[m] = -__builtin_inff();
+      bi[m] = kNoIndex;
     }
-    argmax_finish(a, nwg, red, W);
+    for (int n = tid; n < nrows; n += NT) {
+      const int t = n / RT, rt = n - t * RT;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) argmax_take(bv[m], bi[m], row_sum(t, rt, m) * ig0, row_lo + n);
+    }
+    wg_argmax_rows<MT>(bv, bi, MT, red, W);
+    if (tid < MT) {
+      float* c = a.cand + ((size_t)rb * a.M + tid) * 2;
+      store_coherent(c, bv[0]);
+      store_coherent(c + 1, __int_as_float(bi[0]));
+    }
+    argmax_finish<MT>(a, nwg, red, W);
   } else
   for (int n = tid; n < nrows; n += NT) {
     const int t = n / RT, rt = n - t * RT;
@@ -1019,28 +1058,40 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
     // S == 1 here (the host rejects a K split with this epilogue); x is no
     // longer needed, so its LDS holds the reduction scratch
     float* red = reinterpret_cast<float*>(xs);
-    for (int m = 0; m < M; ++m) {
-      float bv = -__builtin_inff();
-      int bi = kNoIndex;
-      for (int n = tid; n < nrows; n += NT) {
-        const int t = n / RT, rt = n - t * RT;
-        const int rr = rt / QS, jo = rt - rr * QS;
-        const int idx = (rr * (4 * P) + m) * 4 + jo;
-        float v = 0.0f;
-        for (int w = tw0[t]; w <= tw1[t]; ++w) {
-          const int k = t - wft[w];
-          if (k >= 0) v += seg[(w * a.kmax + k) * V + idx];
-        }
-        argmax_take(bv, bi, v * ig0, row_lo + n);
-      }
-      wg_argmax(bv, bi, red, W);
-      if (tid == 0) {
-        float* c = a.cand + ((size_t)rb * M + m) * 2;
-        store_coherent(c, bv);
-        store_coherent(c + 1, __int_as_float(bi));
-      }
+    constexpr int MB = 4 * P;
+    float bv[MB];
+    int bi[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      bv[m] = -__builtin_inff();
+      bi[m] = kNoIndex;
     }
-    argmax_finish(a, nwg, red, W);
+    for (int n = tid; n < nrows; n += NT) {
+      const int t = n / RT, rt = n - t * RT;
+      const int rr = rt / QS, jo = rt - rr * QS;
+      // the logits of weight row n for every activation row m: its task's
+      // segment values at (rr * 4P + m) * 4 + jo, added in wave order
+      float v[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) v[m] = 0.0f;
+      for (int w = tw0[t]; w <= tw1[t]; ++w) {
+        const int k = t - wft[w];
+        if (k < 0) continue;  // a wave without steps
+        const float* sg = seg + (w * a.kmax + k) * V + rr * (4 * P) * 4 + jo;
+#pragma unroll
+        for (int m = 0; m < MB; ++m) v[m] += sg[m * 4];
+      }
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        if (m < M) argmax_take(bv[m], bi[m], v[m] * ig0, row_lo + n);
+    }
+    wg_argmax_rows<MB>(bv, bi, M, red, W);
+    if (tid < M) {
+      float* c = a.cand + ((size_t)rb * M + tid) * 2;
+      store_coherent(c, bv[0]);
+      store_coherent(c + 1, __int_as_float(bi[0]));
+    }
+    argmax_finish<MB>(a, nwg, red, W);
   } else
   // item o = n * 4P + m (rows m >= M are skipped): a constant divisor
   for (int o = tid; o < nrows * 4 * P; o += NT) {
