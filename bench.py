@@ -244,7 +244,8 @@ def bench_extra(dev, stream, cycles=10):
         out[f"down_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
         log(f"[bench] down M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
     # the whole MLP block (gate/up + SwiGLU + down) per call: one persistent
-    # launch, and the same calls forced to two launches
+    # launch (forced under capture), and the same calls in two launches (what
+    # a captured call takes by default)
     H, F = N, K          # the down projection's output and input widths
     nb = min(len(G[0]), len(D[0]))
     for M in (1, 7):
@@ -255,8 +256,10 @@ def bench_extra(dev, stream, cycles=10):
                                             (D[0][i], D[1][i], D[2][i]), x, y=y, workspace=work, stream=s)
                for i in range(nb)]
         b = 2 * weight_bytes(F, H) + weight_bytes(H, F)
-        res = {"one_launch": w4.mlp_one_launch(M, H, F)}
-        for mode, name in ((0, "auto"), (1, "two_launches")):
+        # eager calls take one launch when the shape allows it (mlp_one_launch);
+        # captured calls take two by default: both are timed here under capture
+        res = {"one_launch_eager": w4.mlp_one_launch(M, H, F)}
+        for mode, name in ((2, "one_launch"), (1, "two_launches")):
             w4.mlp_set_options(mode, 1 << 20)
             try:
                 t = graph_time(fns, cycles, stream)
@@ -272,11 +275,11 @@ def bench_extra(dev, stream, cycles=10):
 def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
     """Full-tower decode sweep, one token = one HIP graph replay of
     `layers` x (the MLP block: gate/up + SwiGLU 5120 -> 2 x 17408 and down
-    17408 -> 5120, one persistent launch where the device allows it; q, k, v,
-    o 5120 -> 5120) followed by the 5120 -> 248320 head GEMV with fused greedy
-    argmax (the head alone is also timed with and without it): 321 launches
-    (385 with two-launch MLP blocks) and 14.1 GB of distinct weight
-    allocations per token.  The MLP
+    17408 -> 5120 through w4a16_mlp_swiglu, which takes two launches under
+    capture; q, k, v, o 5120 -> 5120) followed by the 5120 -> 248320 head GEMV
+    with fused greedy argmax (the head alone is also timed with and without
+    it): 385 launches and 14.1 GB of distinct weight allocations per token.
+    The MLP
     chain is wired (SwiGLU output feeds down, down's output feeds the next
     layer's gate/up); q/k/v/o and the head read fixed synthetic activations
     (there is no attention).  Weights per layer are byte-identical replicas of
@@ -346,7 +349,7 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
                                  argmax_us_per_call=t_head_am * 1e6, argmax_gbs=bh / t_head_am / 1e9)
         log(f"[bench] head 5120->{V} M={M}: logits {t_head*1e6:.1f} us ({bh/t_head/1e9:.0f} GB/s), "
             f"fused argmax {t_head_am*1e6:.1f} us ({bh/t_head_am/1e9:.0f} GB/s)")
-        per_layer = 5 if w4.mlp_one_launch(M, H, F) == 1 else 6
+        per_layer = 6  # captured MLP blocks run as two launches (gate/up, down)
         out[f"tower_M{M}"] = dict(ms_per_token=t * 1e3, tokens_per_s=1.0 / t,
                                   launches_per_token=per_layer * layers + 1,
                                   head="fused greedy argmax",

@@ -214,12 +214,15 @@ def workspace_size_mlp(M: int, H: int, F: int) -> int:
 
 
 def mlp_one_launch(M: int, H: int, F: int) -> int:
-    """1: one persistent launch on the current device; 0: two launches; -1: unsupported."""
+    """1: one persistent launch on the current device (for a call that is not
+    being captured into a graph); 0: two launches; -1: unsupported."""
     return int(lib().w4a16_mlp_one_launch(M, H, F))
 
 
 def mlp_set_options(mode: int = 0, spin_limit: int = 1 << 20) -> None:
-    """mode 0: one launch when possible, 1: always two; spin_limit: barrier polls."""
+    """mode 0: one launch when possible, two while the stream is being captured
+    (default); 1: always two; 2: one launch when possible, captured or not;
+    spin_limit: barrier polls."""
     if lib().w4a16_mlp_set_options(int(mode), int(spin_limit)) != 1:
         raise ValueError("invalid MLP options")
 

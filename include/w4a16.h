@@ -173,9 +173,11 @@ w4a16_status_t w4a16_quantize_bf16(const uint16_t* w, uint8_t* wq, uint8_t* ws, 
  * grids to one wave of multiprocessors ("How it works", "Performance"); here,
  * when the two matmuls' launch plans allow it (same kernel family and block
  * size) and the whole grid fits on the device at once, both run in ONE
- * persistent launch with a device-wide barrier between them; otherwise two
- * launches on `stream`.  w4a16_mlp_one_launch() tells which.  The results
- * are bit-identical either way.
+ * persistent launch with a device-wide barrier between them; otherwise, and
+ * by default while `stream` is being captured into a graph (where two
+ * launches measured faster: the barrier costs more than a graph's launch
+ * gap), two launches on `stream`.  w4a16_mlp_one_launch() tells which for an
+ * uncaptured call.  The results are bit-identical either way.
  *   workspace : at least w4a16_workspace_size_mlp(M, H, F) bytes (never 0 for
  *               a supported shape), 256-byte aligned.  Its first
  *               W4A16_MLP_H_OFFSET bytes hold counters and barrier words:
@@ -205,12 +207,15 @@ w4a16_status_t w4a16_mlp_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,
 /* Bytes of workspace w4a16_mlp_swiglu needs (0 = unsupported shape). */
 size_t w4a16_workspace_size_mlp(int M, int H, int F);
 
-/* 1 if w4a16_mlp_swiglu runs this shape in one launch on the current device,
- * 0 if in two, -1 if the shape is unsupported. */
+/* 1 if w4a16_mlp_swiglu runs this shape in one launch on the current device
+ * (for a call on a stream that is not being captured, or under mode 2), 0 if
+ * in two, -1 if the shape is unsupported. */
 int w4a16_mlp_one_launch(int M, int H, int F);
 
 /* Diagnostics and tests (process-wide, not thread-safe): mode 0 = one launch
- * when possible (default), 1 = always two launches; spin_limit = barrier
+ * when possible, two while the stream is being captured (default); 1 =
+ * always two launches; 2 = one launch when possible, captured or not;
+ * spin_limit = barrier
  * polls before a workgroup gives up waiting (default 2^20; 0 makes every
  * workgroup but the last to arrive give up at once).  Returns 1, or 0 for
  * an invalid argument (nothing changed). */

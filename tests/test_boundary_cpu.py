@@ -207,7 +207,9 @@ def test_mlp_workspace_layout(lib):
 
 
 def test_mlp_options(lib):
-    assert lib.w4a16_mlp_set_options(2, 10) == 0
+    assert lib.w4a16_mlp_set_options(3, 10) == 0
+    assert lib.w4a16_mlp_set_options(-1, 10) == 0
+    assert lib.w4a16_mlp_set_options(2, 10) == 1
     assert lib.w4a16_mlp_set_options(0, -1) == 0
     assert lib.w4a16_mlp_set_options(1, 5) == 1
     assert lib.w4a16_mlp_set_options(0, 1 << 20) == 1

@@ -175,7 +175,18 @@ def test_workspace_reused_across_shapes():
         assert counters_zero(work)
 
 
-def test_graph_capture_replays_match_eager():
+@pytest.mark.parametrize("mode", [0, 2])
+def test_graph_capture_replays_match_eager(mode):
+    """Mode 0 captures two launches, mode 2 the one-launch persistent kernel;
+    both must replay to the eager (one-launch) result, bit for bit."""
+    w4.mlp_set_options(mode, 1 << 20)
+    try:
+        _graph_replays_match_eager()
+    finally:
+        w4.mlp_set_options(0, 1 << 20)
+
+
+def _graph_replays_match_eager():
     for M, H, F in [(1, 5120, 17408), (7, 5120, 17408)]:
         host, dev, x = block(600, M, H, F)
         dx = d_bf16(x)
