@@ -129,3 +129,32 @@ def test_run_to_run_identical():
     for _ in range(3):
         again = run(wq, ws, g, x)
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1].view(np.uint32), again[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [3, 5, 13])
+def test_ties_and_nan_rows_on_the_mfma_path(M):
+    """M >= 3 runs on the MFMA kernel, whose epilogue reduces every activation
+    row side by side.  Exact arithmetic as above: for each activation row m
+    but the last, three weight rows hold m's largest possible logit (codes +-6
+    with x[m]'s signs) and the smallest of them must win, with the exact value;
+    the last activation row holds a NaN, so all its logits are NaN and its
+    index is -1."""
+    N, K = 7000, 1024
+    wq, ws, g, x, xi = exact_case(M, N, K, 30 + M)
+    rng = np.random.default_rng(40 + M)
+    planted = rng.choice(N, size=(M - 1, 3), replace=False)
+    for m in range(M - 1):
+        w = winner_row(xi[m], K)
+        for r in planted[m]:
+            wq[r] = w
+    x = x.copy()
+    x[M - 1, 5] = 0x7FC0                      # a bf16 NaN
+    idx, val = run(wq, ws, g, x)
+    ref, a = oracle.gemm(wq, ws, g, x, M, N, K, nthreads=NTHREADS)
+    for m in range(M - 1):
+        best = np.flatnonzero(ref[m] == ref[m].max())
+        assert set(planted[m]) <= set(best), (M, m)      # the planted rows are maxima
+        want = int(best[0])                              # ties: the smallest index
+        assert idx[m] == want and val[m] == ref[m, want], (M, m, idx[m], want)
+    assert np.isnan(ref[M - 1]).all()
+    assert idx[M - 1] == -1, idx[M - 1]
