@@ -38,13 +38,14 @@ TRAFFIC_FILE = os.path.join(PROFILES, "traffic_square_m1.json")
 
 
 def kernel_source_hash():
-    """Hash of the HIP sources: a stored traffic measurement is used only if it
-    was taken on exactly these kernels."""
+    """Hash of the matmul library's HIP sources: a stored traffic measurement is
+    used only if it was taken on exactly these kernels (the calibration kernel's
+    source, calib.hip, is not part of them)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_scaled_fp4_w4a16_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
+        if name.endswith((".hip", ".h")) and not name.startswith("calib"):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -370,6 +371,46 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
     return out
 
 
+def calibration(dev, stream, copies, call_bytes=5120 * 5120 // 2 + 5120 * 5120 // 16):
+    """Achievable HBM read rates, from a plain 128-bit non-temporal streaming
+    read (libw4a16_calib.so, not the matmul library): once on a 4 GiB buffer
+    (32 workgroups of 1024 threads per CU: the fastest launch shape of a sweep
+    on MI355X, 6.6-7.0 TB/s), and over `copies` buffers of one
+    square call's weight bytes cycled like the weight copies, with the GEMV's
+    grid (one workgroup of 512 threads per CU), in a HIP graph like the
+    benchmark.  The second rate includes the same per-call fixed costs."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "block_scaled_fp4_w4a16_amd", "libw4a16_calib.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m block_scaled_fp4_w4a16_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.w4a16_calib_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.w4a16_calib_stream_read.restype = ctypes.c_int
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def read(buf, nbytes, grid, block, s):
+        st = lib.w4a16_calib_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()),
+                                         grid, block, ctypes.c_void_p(s.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"calibration read failed ({st})")
+
+    big_bytes = 4 << 30
+    big = torch.ones(big_bytes, dtype=torch.uint8, device=dev)
+    t_big = graph_time([lambda s: read(big, big_bytes, 32 * cus, 1024, s)], 10, stream)
+    del big
+    bufs = [torch.ones(call_bytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    t_call = graph_time([lambda s, i=i: read(bufs[i], call_bytes, cus, 512, s) for i in range(copies)], 10, stream)
+    del bufs
+    return {"kind": "plain 128-bit non-temporal streaming read (libw4a16_calib.so)",
+            "stream_4gib_gbs": round(big_bytes / t_big / 1e9, 1),
+            "call_sized_bytes": call_bytes, "call_sized_copies": copies,
+            "call_sized_us_per_call": round(t_call * 1e6, 3),
+            "call_sized_gbs": round(call_bytes / t_call / 1e9, 1)}
+
+
 def cpu_baseline(seconds_target=12.0):
     """The CPU oracle timed on a bounded sample of the square workload."""
     import oracle
@@ -448,6 +489,8 @@ def main():
     ap.add_argument("--tower", action="store_true",
                     help="also time the full-tower decode sweep (64 layers + head, 14.1 GB, M = 1 and 7)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the achievable-read-bandwidth calibration")
     ap.add_argument("--mode", choices=["bench", "copy", "ingest-pmc"], default="bench",
                     help="copy: run only the PMC calibration copy kernel; ingest-pmc: turn rocprofv3 "
                          "FETCH_SIZE/WRITE_SIZE outputs (--pmc-dir) into profiles/traffic_square_m1.json")
@@ -474,6 +517,12 @@ def main():
     log(f"[bench] square (graph replay): {r['per_call']*1e6:.3f} us/call, {r['gbs']:.1f} GB/s; "
         f"eager: {r['eager_per_call']*1e6:.3f} us/call, {r['eager_gbs']:.1f} GB/s; "
         f"M=7: {r['m7_per_call']*1e6:.3f} us/call, {r['m7_gbs']:.1f} GB/s")
+    cal = None if args.no_calibration else calibration(dev, stream, r["copies"])
+    if cal is not None:
+        cal["value_frac_of_stream"] = round(r["gbs"] / cal["stream_4gib_gbs"], 4)
+        cal["value_frac_of_call_sized"] = round(r["gbs"] / cal["call_sized_gbs"], 4)
+        log(f"[bench] calibration: streaming read {cal['stream_4gib_gbs']} GB/s (4 GiB), "
+            f"{cal['call_sized_gbs']} GB/s ({cal['call_sized_us_per_call']} us per 14.7 MB call)")
     extra = bench_extra(dev, stream) if args.extra else None
     if args.tower:
         extra = dict(extra or {}, **bench_tower(dev, stream))
@@ -505,6 +554,8 @@ def main():
         # block of M = 7 activation rows (not the `value`)
         "square_M7": {"us_per_call": round(r["m7_per_call"] * 1e6, 3), "gbs": round(r["m7_gbs"], 2),
                       "frac": round(r["m7_gbs"] / HBM_PEAK_GBS, 4), "calls_timed": 10 * r["copies"]},
+        # achievable read rates on this box: `value` against them is "% of achievable"
+        "calibration": cal,
     }
     if extra is not None:
         line["extra"] = extra

@@ -215,3 +215,25 @@ def test_mlp_options(lib):
     assert lib.w4a16_mlp_set_options(0, 1 << 20) == 1
     with pytest.raises(ValueError):
         w4.mlp_set_options(3)
+
+
+def test_calibration_library_rejects_bad_arguments_without_a_gpu():
+    """The benchmark's HBM calibration library (not part of the matmul ABI):
+    it loads, exports its one entry point, and rejects bad arguments before
+    touching the device."""
+    import ctypes
+    import os
+    path = os.path.join(os.path.dirname(w4.library_path()), "libw4a16_calib.so")
+    lib = ctypes.CDLL(path)
+    f = lib.w4a16_calib_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                  ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    P = 1 << 20                                   # a 16-byte aligned stand-in address
+    assert f(0, 1024, P, 1, 64, None) != 0        # null buffer
+    assert f(P, 1024, 0, 1, 64, None) != 0        # null sink
+    assert f(P, 1000, P, 1, 64, None) != 0        # size not a multiple of 16
+    assert f(P + 4, 1024, P, 1, 64, None) != 0    # misaligned buffer
+    assert f(P, 1024, P, 0, 64, None) != 0        # empty grid
+    assert f(P, 1024, P, 1, 2048, None) != 0      # block above 1024
+    assert f(P, 1024, P, 1, 100, None) != 0       # block not whole waves
