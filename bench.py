@@ -466,7 +466,8 @@ def ingest_pmc(d):
     total = 0.0
     for ctr, copy_pred in (("FETCH_SIZE", lambda n: "copyBuffer" in n),
                            ("WRITE_SIZE", lambda n: "copyBuffer" in n)):
-        gemm = statistics.median(values(f"pmc_bench_{ctr}", lambda n: "k_gemm" in n))
+        # the square GEMV at M = 1 (the run also has the M = 7 calls, on the MFMA kernel)
+        gemm = statistics.median(values(f"pmc_bench_{ctr}", lambda n: "k_gemm_valu" in n))
         cal = statistics.median(values(f"pmc_copy_{ctr}", copy_pred))
         factor = copy_kib / cal
         out[ctr] = {"gemm_kib_per_dispatch": gemm, "copy_kib_per_dispatch": cal, "factor": round(factor, 4),
