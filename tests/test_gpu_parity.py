@@ -151,10 +151,13 @@ def test_tiny_config():
     check_gemm(wq, ws, g, synth.activations(c["seed_x"], 1, c["K"]), 1, c["N"], c["K"], "tiny")
 
 
-def test_square_config():
+@pytest.mark.parametrize("M", [1, 7])
+def test_square_config(M):
+    """M = 1 is the benchmark's value; M = 7, a verify block on the same
+    weights and seeds, is the second figure its line reports."""
     c = synth.CONFIGS["square"]
     wq, ws, g = weights(c["seed_w"], c["N"], c["K"])
-    check_gemm(wq, ws, g, synth.activations(c["seed_x"], 1, c["K"]), 1, c["N"], c["K"], "square")
+    check_gemm(wq, ws, g, synth.activations(c["seed_x"], M, c["K"]), M, c["N"], c["K"], f"square M={M}")
 
 
 @pytest.mark.parametrize("M", [1, 7])
