@@ -267,15 +267,19 @@ def bench_extra(dev, stream, cycles=10):
                                             (D[0][i], D[1][i], D[2][i]), x, y=y, workspace=work, stream=s)
                for i in range(nb)]
         b = 2 * weight_bytes(F, H) + weight_bytes(H, F)
-        # eager calls take one launch when the shape allows it (mlp_one_launch);
-        # captured calls take two by default: both are timed here under capture
-        res = {"one_launch_eager": w4.mlp_one_launch(M, H, F)}
-        for mode, name in ((2, "one_launch"), (1, "two_launches")):
-            w4.mlp_set_options(mode, 1 << 20)
-            try:
-                t = graph_time(fns, cycles, stream)
-            finally:
-                w4.mlp_set_options(0, 1 << 20)
+        # captured calls take two launches; the one-launch (cooperative) path
+        # runs only for eager calls, so both are also timed eagerly
+        res = {"one_launch_possible": w4.mlp_one_launch(M, H, F)}
+        t = graph_time(fns, cycles, stream)
+        res["two_launches_graph"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9,
+                                         pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
+        log(f"[bench] mlp block M={M} (two launches, graph): {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
+        for one, name in ((True, "one_launch_eager"), (False, "two_launches_eager")):
+            efns = [lambda i=i: w4.mlp_swiglu((G[0][i], G[1][i], G[2][i]), (U[0][i], U[1][i], U[2][i]),
+                                              (D[0][i], D[1][i], D[2][i]), x, y=y, workspace=work,
+                                              stream=stream, one_launch=one)
+                    for i in range(nb)]
+            t = time_calls(efns, cycles, 2, stream)
             res[name] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
             log(f"[bench] mlp block M={M} ({name}): {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
         out[f"mlp_M{M}"] = res

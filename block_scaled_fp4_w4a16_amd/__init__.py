@@ -75,14 +75,13 @@ def lib():
     L.w4a16_status_string.restype = ctypes.c_char_p
     L.w4a16_abi_version.argtypes = []
     L.w4a16_abi_version.restype = I
-    L.w4a16_mlp_swiglu.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, P, Z, P]
+    L.w4a16_mlp_swiglu.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, P, Z,
+                                   ctypes.POINTER(MlpOptions), P]
     L.w4a16_mlp_swiglu.restype = I
     L.w4a16_workspace_size_mlp.argtypes = [I, I, I]
     L.w4a16_workspace_size_mlp.restype = Z
     L.w4a16_mlp_one_launch.argtypes = [I, I, I]
     L.w4a16_mlp_one_launch.restype = I
-    L.w4a16_mlp_set_options.argtypes = [I, I]
-    L.w4a16_mlp_set_options.restype = I
     _lib = L
     return L
 
@@ -214,17 +213,27 @@ def workspace_size_mlp(M: int, H: int, F: int) -> int:
 
 
 def mlp_one_launch(M: int, H: int, F: int) -> int:
-    """1: one persistent launch on the current device (for a call that is not
-    being captured into a graph); 0: two launches; -1: unsupported."""
+    """1: the block can run in one persistent launch on the current device
+    (when asked to, outside graph capture); 0: always two launches;
+    -1: unsupported."""
     return int(lib().w4a16_mlp_one_launch(M, H, F))
 
 
-def mlp_set_options(mode: int = 0, spin_limit: int = 1 << 20) -> None:
-    """mode 0: one launch when possible, two while the stream is being captured
-    (default); 1: always two; 2: one launch when possible, captured or not;
-    spin_limit: barrier polls."""
-    if lib().w4a16_mlp_set_options(int(mode), int(spin_limit)) != 1:
-        raise ValueError("invalid MLP options")
+MLP_TWO_LAUNCHES, MLP_ONE_LAUNCH = 0, 1
+
+
+class MlpOptions(ctypes.Structure):
+    """w4a16_mlp_options_t: per-call settings of w4a16_mlp_swiglu."""
+    _fields_ = [("launch", ctypes.c_int), ("spin_limit", ctypes.c_int)]
+
+
+def mlp_timed_out(workspace) -> bool:
+    """Whether a one-launch call on this workspace stopped waiting at its
+    barrier (its y is then undefined).  Reads the flag after the device's
+    queued work: synchronises."""
+    torch.cuda.synchronize(workspace.device)
+    flag = workspace[MLP_TIMEOUT_OFFSET:MLP_TIMEOUT_OFFSET + 4].view(torch.int32).item()
+    return flag != 0
 
 
 def new_workspace_mlp(M: int, H: int, F: int, device):
@@ -235,9 +244,13 @@ def new_workspace_mlp(M: int, H: int, F: int, device):
     return torch.zeros(need, dtype=torch.uint8, device=device)
 
 
-def mlp_swiglu(gate, up, down, x, y=None, workspace=None, stream=None):
+def mlp_swiglu(gate, up, down, x, y=None, workspace=None, stream=None, one_launch=False,
+               spin_limit=-1):
     """y[M, H] = bf16(bf16(silu(x @ Wg^T) * (x @ Wu^T)) @ Wd^T): one MLP block.
-    gate, up, down: (wq, ws, g) tuples; Wg, Wu are [F][H], Wd is [H][F]."""
+    gate, up, down: (wq, ws, g) tuples; Wg, Wu are [F][H], Wd is [H][F].
+    one_launch: run both matmuls in one cooperative persistent launch when
+    the shape and the stream allow it (bit-identical to two launches);
+    spin_limit: the barrier's poll limit (< 0: the library default)."""
     F, H = _weights(*gate, "gate ")
     if _weights(*up, "up ") != (F, H):
         raise ValueError("gate and up weights must have the same shape")
@@ -257,8 +270,9 @@ def mlp_swiglu(gate, up, down, x, y=None, workspace=None, stream=None):
     else:
         _check(workspace, "workspace", workspace.dtype, None)
     wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    opts = MlpOptions(MLP_ONE_LAUNCH if one_launch else MLP_TWO_LAUNCHES, int(spin_limit))
     st = lib().w4a16_mlp_swiglu(*[_ptr(t) for t in (*gate, *up, *down)], _ptr(x), _ptr(y), M, H, F,
-                                _ptr(workspace), wbytes, _stream(stream))
+                                _ptr(workspace), wbytes, ctypes.byref(opts), _stream(stream))
     if st != OK:
         raise W4A16Error(st, "w4a16_mlp_swiglu")
     return y

@@ -378,15 +378,8 @@ const MlpKernEntry kMlpKernels[] = {
     W4A16_MLPM(1) W4A16_MLPM(2) W4A16_MLPM(3) W4A16_MLPM(4)
     W4A16_MLPM(5) W4A16_MLPM(6) W4A16_MLPM(7) W4A16_MLPM(8)};
 
-// Library options for the MLP entry point (diagnostics and tests).
-// 0: one launch when possible, except while the stream is being captured
-// into a graph; 1: always two launches; 2: one launch when possible, captured
-// or not.  Under graph replay two launches measured faster on MI355X (MLP
-// block 5120 -> 2 x 17408 -> 5120: M = 1 28.6 vs 29.5 us, M = 7 40.1 vs
-// 40.4 us): the device-wide barrier costs more than a graph's launch gap.
-// Eager callers still save a host-side launch with one.
-int g_mlp_mode = 0;
-int g_mlp_spin = 1 << 20;      // barrier polls before a workgroup gives up
+// Default barrier poll limit of the one-launch MLP kernel.
+constexpr int kMlpSpinDefault = 1 << 20;
 
 struct MlpPlan {
   Plan p1, p2;              // gate/up (N = F, K = H) and down (N = H, K = F)
@@ -411,7 +404,7 @@ MlpPlan plan_mlp(int M, int H, int F) {
   // depth, h addressable by 32-bit buffer offsets, and every workgroup of the
   // grid resident at once (the barrier waits for all of them)
   const Plan &a = mp.p1, &b = mp.p2;
-  if (g_mlp_mode == 1 || a.mfma != b.mfma || a.W != b.W || a.LB != b.LB || a.D != b.D ||
+  if (a.mfma != b.mfma || a.W != b.W || a.LB != b.LB || a.D != b.D ||
       (size_t)M * F * 2 >= ((size_t)1 << 31))
     return mp;
   const int rows = a.mfma ? (M + 3) / 4 : M;
@@ -445,12 +438,17 @@ void mlp_check_resident(MlpPlan& mp) {
 }
 
 w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace,
-                       size_t workspace_bytes, hipStream_t stream) {
+                       size_t workspace_bytes, const w4a16_mlp_options_t* opt,
+                       hipStream_t stream) {
   const int M = up0.M, H = up0.K, F = up0.N;
   MlpPlan mp = plan_mlp(M, H, F);
   if (mp.p1.S == 0 || mp.p1.lds > kMaxLds || mp.p2.lds > kMaxLds) return W4A16_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < mp.ws) return W4A16_ERR_INVALID_VALUE;
   if (!aligned(workspace, 256)) return W4A16_ERR_UNSUPPORTED;
+  const int launch = opt ? opt->launch : W4A16_MLP_TWO_LAUNCHES;
+  if (launch != W4A16_MLP_TWO_LAUNCHES && launch != W4A16_MLP_ONE_LAUNCH)
+    return W4A16_ERR_INVALID_VALUE;
+  const int spin = (opt && opt->spin_limit >= 0) ? opt->spin_limit : kMlpSpinDefault;
   char* w = static_cast<char*>(workspace);
   uint16_t* h = reinterpret_cast<uint16_t*>(w + kMlpHOffset);
   MatArgs up = up0, down = down0;
@@ -459,13 +457,15 @@ w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace
   prepare(up, mp.p1, reinterpret_cast<int*>(w), reinterpret_cast<float*>(w + mp.part1));
   prepare(down, mp.p2, reinterpret_cast<int*>(w + kCounterBytes),
           reinterpret_cast<float*>(w + mp.part2));
-  mlp_check_resident(mp);
-  if (mp.k && g_mlp_mode == 0) {
+  if (launch == W4A16_MLP_ONE_LAUNCH) {
+    mlp_check_resident(mp);
+    // a cooperative launch is not taken while the stream is being captured
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
-      mp.k = nullptr;  // being captured: two launches (see g_mlp_mode)
+    if (mp.k && (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone))
+      mp.k = nullptr;
+  } else {
+    mp.k = nullptr;
   }
-  hipError_t e;
   if (mp.k) {
     MlpArgs m{};
     m.up = up;
@@ -475,15 +475,18 @@ w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace
     m.nrb2 = mp.p2.nrb;
     m.nwg2 = mp.p2.nrb * mp.p2.S;
     m.bar = reinterpret_cast<int*>(w + kMlpBarrierOffset);
-    m.spin_limit = g_mlp_spin;
+    m.spin_limit = spin;
     void* argv[] = {&m};
-    e = hipLaunchKernel(mp.k->fn, dim3((unsigned)mp.grid), dim3((unsigned)(mp.p1.W * 64)), argv,
-                        mp.lds, stream);
-    if (e == hipSuccess) e = hipGetLastError();
-  } else {
-    e = dispatch(mp.p1, kEpiSwiglu, stream, up);
-    if (e == hipSuccess) e = dispatch(mp.p2, kEpiPlain, stream, down);
+    // cooperative: every workgroup resident at once, or the launch is
+    // refused (nothing enqueued) and the block runs as two kernels below
+    const hipError_t e = hipLaunchCooperativeKernel(mp.k->fn, dim3((unsigned)mp.grid),
+                                                    dim3((unsigned)(mp.p1.W * 64)), argv, mp.lds,
+                                                    stream);
+    if (e == hipSuccess) return W4A16_OK;
+    (void)hipGetLastError();  // clear the refused launch's error
   }
+  hipError_t e = dispatch(mp.p1, kEpiSwiglu, stream, up);
+  if (e == hipSuccess) e = dispatch(mp.p2, kEpiPlain, stream, down);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
@@ -661,7 +664,7 @@ w4a16_status_t w4a16_mlp_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,
                                 const float* g_up, const uint8_t* wq_down, const uint8_t* ws_down,
                                 const float* g_down, const uint16_t* x, uint16_t* y, int M, int H,
                                 int F, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                const w4a16_mlp_options_t* options, hipStream_t stream) {
   if (!wq_gate || !ws_gate || !g_gate || !wq_up || !ws_up || !g_up || !wq_down || !ws_down ||
       !g_down || !x || !y)
     return W4A16_ERR_INVALID_VALUE;
@@ -691,7 +694,7 @@ w4a16_status_t w4a16_mlp_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,
   down.M = M;
   down.N = H;
   down.K = F;
-  return run_mlp(up, down, workspace, workspace_bytes, stream);
+  return run_mlp(up, down, workspace, workspace_bytes, options, stream);
 }
 
 size_t w4a16_workspace_size_mlp(int M, int H, int F) {
@@ -707,13 +710,6 @@ int w4a16_mlp_one_launch(int M, int H, int F) {
   if (mp.p1.S == 0 || mp.p1.lds > kMaxLds || mp.p2.lds > kMaxLds) return -1;
   mlp_check_resident(mp);
   return mp.k ? 1 : 0;
-}
-
-int w4a16_mlp_set_options(int mode, int spin_limit) {
-  if (mode < 0 || mode > 2 || spin_limit < 0) return 0;
-  g_mlp_mode = mode;
-  g_mlp_spin = spin_limit;
-  return 1;
 }
 
 const char* w4a16_status_string(w4a16_status_t status) {

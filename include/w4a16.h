@@ -77,9 +77,12 @@ typedef enum {
  *               zero again, so one zero-fill serves any number of calls, of
  *               any shapes, made one after another.  The partial sums after
  *               them need no initialisation.
- * Accuracy contract: |y - y_exact| <= 1e-2 * sum_k |x[m][k] * W[n][k]| + 1e-6
- * for every (m, n).  Defined by the page's schema and "NVFP4 W4A16" format
- * (FlashRT, "Qwen3.6-27B NVFP4 on RTX 5090", section 1).
+ * The operation is the "NVFP4 W4A16" matmul of FlashRT, "Qwen3.6-27B NVFP4
+ * on RTX 5090", section 1 (weights in the schema above, bf16 activations).
+ * Accuracy contract (this library's own target; the pages state no numeric
+ * tolerance): |y - y_exact| <= 1e-2 * sum_k |x[m][k] * W[n][k]| + 1e-6 for
+ * every (m, n).  On inputs whose fp32 sums are exact (integer x, power-of-two
+ * g and scales) y equals y_exact rounded once to bf16.
  */
 w4a16_status_t w4a16_gemm(const uint8_t* wq, const uint8_t* ws, const float* g,
                           const uint16_t* x, uint16_t* y, int M, int N, int K,
@@ -152,9 +155,9 @@ w4a16_status_t w4a16_dequant(const uint8_t* wq, const uint8_t* ws, const float* 
  *               aligned, no initialisation needed.
  *   Inputs are expected finite: NaN elements are ignored by the maxima, and an
  *   infinite element makes g = 0 and every code 0.
- * For converting a higher-precision checkpoint at load time (FlashRT §0/§1
- * convert checkpoints to NVFP4 before serving; qwentin packs 4-bit weights on
- * the GPU at conversion).
+ * For converting a higher-precision checkpoint at load time: FlashRT (sections
+ * 0 and 1) serves checkpoints already in this schema and converts its
+ * drafter head to NVFP4 when loading it.
  */
 w4a16_status_t w4a16_quantize(const float* w, uint8_t* wq, uint8_t* ws, float* g, int N, int K,
                               void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -170,14 +173,17 @@ w4a16_status_t w4a16_quantize_bf16(const uint16_t* w, uint8_t* wq, uint8_t* ws, 
  * g), x : bf16 [M][H], y : bf16 [M][H].  Same alignment rules as w4a16_gemm
  * for every matrix; H % 256 == 0 and F % 256 == 0; 1 <= M <= 32.
  * The qwentin README lists a persistent-MLP GEMV among its kernels and sizes
- * grids to one wave of multiprocessors ("How it works", "Performance"); here,
- * when the two matmuls' launch plans allow it (same kernel family and block
- * size) and the whole grid fits on the device at once, both run in ONE
- * persistent launch with a device-wide barrier between them; otherwise, and
- * by default while `stream` is being captured into a graph (where two
- * launches measured faster: the barrier costs more than a graph's launch
- * gap), two launches on `stream`.  w4a16_mlp_one_launch() tells which for an
- * uncaptured call.  The results are bit-identical either way.
+ * grids to one wave of multiprocessors ("How it works", "Performance").
+ * By default the block runs as two kernels on `stream`.  With options->launch
+ * = W4A16_MLP_ONE_LAUNCH both matmuls run in ONE persistent launch with a
+ * device-wide barrier between them, when the two launch plans allow it (same
+ * kernel family and block size, see w4a16_mlp_one_launch) and the stream is
+ * not being captured into a graph.  That launch is cooperative: the runtime
+ * either makes every workgroup resident at once or refuses it, and a refused
+ * launch falls back to the two kernels.  The results are bit-identical
+ * either way.
+ *   options   : NULL for the defaults, else per-call settings (below); the
+ *               library keeps no option state between calls.
  *   workspace : at least w4a16_workspace_size_mlp(M, H, F) bytes (never 0 for
  *               a supported shape), 256-byte aligned.  Its first
  *               W4A16_MLP_H_OFFSET bytes hold counters and barrier words:
@@ -185,41 +191,37 @@ w4a16_status_t w4a16_quantize_bf16(const uint16_t* w, uint8_t* wq, uint8_t* ws, 
  *               them zero, except the barrier's generation word (the int at
  *               W4A16_MLP_GENERATION_OFFSET), which may hold any value and
  *               changes with every one-launch call.  h is left at byte
- *               offset W4A16_MLP_H_OFFSET
- *               (bf16 [M][F]).  The int at byte offset
- *               W4A16_MLP_TIMEOUT_OFFSET becomes 1 if a workgroup of the
- *               one-launch kernel stopped waiting at the barrier after its
- *               poll limit (the grid was not all resident, e.g. another
- *               process held the device): y of that call is then undefined;
- *               the flag stays set until the caller clears it.  Calls that
- *               share a workspace must not overlap in time.
+ *               offset W4A16_MLP_H_OFFSET (bf16 [M][F]).  The barrier waits
+ *               at most options->spin_limit polls per workgroup: if one
+ *               stops waiting (only a deliberately tiny limit can make that
+ *               happen, since the launch is cooperative), the int at byte
+ *               offset W4A16_MLP_TIMEOUT_OFFSET becomes 1 and y of that call
+ *               is undefined; the flag stays set until the caller clears it.
+ *               Calls that share a workspace must not overlap in time.
  */
 #define W4A16_MLP_H_OFFSET 10240
 #define W4A16_MLP_GENERATION_OFFSET 9344
 #define W4A16_MLP_TIMEOUT_OFFSET 9472
+#define W4A16_MLP_TWO_LAUNCHES 0
+#define W4A16_MLP_ONE_LAUNCH 1
+typedef struct {
+  int launch;      /* W4A16_MLP_TWO_LAUNCHES (default) or W4A16_MLP_ONE_LAUNCH */
+  int spin_limit;  /* barrier polls before a workgroup stops waiting; < 0 = 2^20 */
+} w4a16_mlp_options_t;
 w4a16_status_t w4a16_mlp_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,
                                 const float* g_gate, const uint8_t* wq_up, const uint8_t* ws_up,
                                 const float* g_up, const uint8_t* wq_down, const uint8_t* ws_down,
                                 const float* g_down, const uint16_t* x, uint16_t* y, int M, int H,
                                 int F, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream);
+                                const w4a16_mlp_options_t* options, hipStream_t stream);
 
 /* Bytes of workspace w4a16_mlp_swiglu needs (0 = unsupported shape). */
 size_t w4a16_workspace_size_mlp(int M, int H, int F);
 
-/* 1 if w4a16_mlp_swiglu runs this shape in one launch on the current device
- * (for a call on a stream that is not being captured, or under mode 2), 0 if
- * in two, -1 if the shape is unsupported. */
+/* 1 if w4a16_mlp_swiglu can run this shape in one launch on the current
+ * device (the plans match and the whole grid fits on the device at once), 0
+ * if it always takes two, -1 if the shape is unsupported. */
 int w4a16_mlp_one_launch(int M, int H, int F);
-
-/* Diagnostics and tests (process-wide, not thread-safe): mode 0 = one launch
- * when possible, two while the stream is being captured (default); 1 =
- * always two launches; 2 = one launch when possible, captured or not;
- * spin_limit = barrier
- * polls before a workgroup gives up waiting (default 2^20; 0 makes every
- * workgroup but the last to arrive give up at once).  Returns 1, or 0 for
- * an invalid argument (nothing changed). */
-int w4a16_mlp_set_options(int mode, int spin_limit);
 
 /* Bytes of workspace w4a16_quantize[_bf16] needs (0 = unsupported shape). */
 size_t w4a16_quantize_workspace_size(int N, int K);
@@ -235,7 +237,7 @@ size_t w4a16_workspace_size_gate_up(int M, int N, int K);
 const char* w4a16_status_string(w4a16_status_t status);
 
 /* ABI version of this header: bumped on any incompatible change. */
-#define W4A16_ABI_VERSION 3
+#define W4A16_ABI_VERSION 4
 int w4a16_abi_version(void);
 
 #ifdef __cplusplus

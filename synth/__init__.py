@@ -140,6 +140,32 @@ def random_bytes(seed: int, shape) -> np.ndarray:
     return np.random.default_rng(seed).integers(0, 256, size=shape, dtype=np.uint8)
 
 
+# ---- inputs on which fp32 accumulation is exact --------------------------------
+# Scale bytes for exact-arithmetic inputs.  POW2: the E4M3FN codes of 0.5, 1, 2
+# and 4 (exponent field 6..9, mantissa 0); MANT: the eight codes with exponent
+# field 7, i.e. 1 + m/8 for m = 0..7.  The tests check these values against the
+# oracle's decoder; this module only stores bytes.
+EXACT_SCALES = {
+    "pow2": np.array([0x30, 0x38, 0x40, 0x48], dtype=np.uint8),
+    "mant": np.arange(0x38, 0x40, dtype=np.uint8),
+}
+
+
+def exact_weights(seed: int, N: int, K: int, scales: str = "pow2"):
+    """Uniformly random code bytes and block scales drawn per (row, block) from
+    EXACT_SCALES[scales]: (wq u8 [N][K/2], ws u8 [N][K/16])."""
+    rng = np.random.default_rng(seed)
+    wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    pick = rng.integers(0, EXACT_SCALES[scales].size, size=(N, K // 16))
+    return wq, EXACT_SCALES[scales][pick]
+
+
+def integer_activations(seed: int, M: int, K: int, lo: int = -2, hi: int = 2) -> np.ndarray:
+    """x with integer values drawn uniformly from [lo, hi], as bf16 bits [M][K]."""
+    rng = np.random.default_rng(seed)
+    return bf16_bits(rng.integers(lo, hi + 1, size=(M, K)).astype(np.float32))
+
+
 # Benchmark configurations: name -> dict(K, N, Ms, seeds, copies)
 CONFIGS = {
     "tiny": dict(K=256, N=512, Ms=(1,), seed_w=11, seed_x=12, copies=1),

@@ -33,8 +33,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for n in ("w4a16_gemm", "w4a16_gemm_gate_up_swiglu", "w4a16_dequant", "w4a16_workspace_size",
               "w4a16_workspace_size_gate_up", "w4a16_status_string", "w4a16_abi_version",
-              "w4a16_mlp_swiglu", "w4a16_workspace_size_mlp", "w4a16_mlp_one_launch",
-              "w4a16_mlp_set_options"):
+              "w4a16_mlp_swiglu", "w4a16_workspace_size_mlp", "w4a16_mlp_one_launch"):
         assert n in names
 
 
@@ -45,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.w4a16_abi_version() == 3
+    assert lib.w4a16_abi_version() == 4
     for st in (0, 1, 2, 3):
         assert len(w4.status_string(st)) > 0
     assert w4.status_string(99) == "unknown status"
@@ -167,10 +166,11 @@ def test_argmax_argument_checks(lib):
 
 # ---- MLP block -----------------------------------------------------------------
 
-def call_mlp(lib, ptrs=None, M=1, H=256, F=512, work=P, wbytes=1 << 30):
+def call_mlp(lib, ptrs=None, M=1, H=256, F=512, work=P, wbytes=1 << 30, opts=None):
     p = dict(wq_g=P, ws_g=P, g_g=P, wq_u=P, ws_u=P, g_u=P, wq_d=P, ws_d=P, g_d=P, x=P, y=P)
     p.update(ptrs or {})
-    return lib.w4a16_mlp_swiglu(*p.values(), M, H, F, work, wbytes, None)
+    return lib.w4a16_mlp_swiglu(*p.values(), M, H, F, work, wbytes,
+                                None if opts is None else ctypes.byref(opts), None)
 
 
 def test_mlp_argument_checks(lib):
@@ -206,15 +206,16 @@ def test_mlp_workspace_layout(lib):
     assert lib.w4a16_mlp_one_launch(33, 256, 512) == -1
 
 
-def test_mlp_options(lib):
-    assert lib.w4a16_mlp_set_options(3, 10) == 0
-    assert lib.w4a16_mlp_set_options(-1, 10) == 0
-    assert lib.w4a16_mlp_set_options(2, 10) == 1
-    assert lib.w4a16_mlp_set_options(0, -1) == 0
-    assert lib.w4a16_mlp_set_options(1, 5) == 1
-    assert lib.w4a16_mlp_set_options(0, 1 << 20) == 1
-    with pytest.raises(ValueError):
-        w4.mlp_set_options(3)
+def test_mlp_options_are_per_call_and_checked(lib):
+    # an unknown launch mode is rejected before anything is enqueued; there is
+    # no process-wide option setter any more
+    assert call_mlp(lib, opts=w4.MlpOptions(2, -1)) == w4.ERR_INVALID_VALUE
+    assert call_mlp(lib, opts=w4.MlpOptions(-1, -1)) == w4.ERR_INVALID_VALUE
+    assert not hasattr(lib, "w4a16_mlp_set_options")
+    hdr = open(HEADER).read()
+    assert "w4a16_mlp_options_t" in hdr and "set_options" not in hdr
+    assert re.search(r"#define W4A16_MLP_TWO_LAUNCHES 0\b", hdr)
+    assert re.search(r"#define W4A16_MLP_ONE_LAUNCH 1\b", hdr)
 
 
 def test_calibration_library_rejects_bad_arguments_without_a_gpu():

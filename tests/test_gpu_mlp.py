@@ -4,7 +4,7 @@ output against oracle.mlp_bound, the one-launch and two-launch paths against
 each other bit for bit, h against the gate/up entry point bit for bit, the
 barrier's time-out path (forced from the host with a poll limit of 0, so every
 kernel still runs to its end), workspace reuse across shapes and HIP-graph
-replays."""
+replays.  The launch mode is a per-call option."""
 import os
 import sys
 
@@ -32,9 +32,7 @@ def _device():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     w4.lib()
-    w4.mlp_set_options(0, 1 << 20)
     yield
-    w4.mlp_set_options(0, 1 << 20)
 
 
 def d_u8(a):
@@ -95,16 +93,12 @@ def check(y, host, x, M, H, F, ctx):
                              f"gpu {got[i]!r} ref {out['y'][i]!r} bound {bound[i]!r}")
 
 
-def run(dev, x_bits, M, H, F, mode, work=None):
-    w4.mlp_set_options(mode, 1 << 20)
-    try:
-        dx = d_bf16(x_bits)
-        if work is None:
-            work = w4.new_workspace_mlp(M, H, F, "cuda")
-        y = w4.mlp_swiglu(*dev, dx, workspace=work)
-        torch.cuda.synchronize()
-    finally:
-        w4.mlp_set_options(0, 1 << 20)
+def run(dev, x_bits, M, H, F, one_launch, work=None):
+    dx = d_bf16(x_bits)
+    if work is None:
+        work = w4.new_workspace_mlp(M, H, F, "cuda")
+    y = w4.mlp_swiglu(*dev, dx, workspace=work, one_launch=one_launch)
+    torch.cuda.synchronize()
     return y, work
 
 
@@ -117,8 +111,8 @@ SHAPES = [(1, 512, 1024), (2, 256, 768), (3, 512, 512), (4, 512, 1024), (5, 256,
 def test_mlp_matches_oracle_both_paths(M, H, F):
     say(f"[mlp] M={M} H={H} F={F} one_launch={w4.mlp_one_launch(M, H, F)}")
     host, dev, x = block(100 + M, M, H, F)
-    y1, work1 = run(dev, x, M, H, F, mode=0)
-    y2, work2 = run(dev, x, M, H, F, mode=1)
+    y1, work1 = run(dev, x, M, H, F, one_launch=True)
+    y2, work2 = run(dev, x, M, H, F, one_launch=False)
     check(y1, host, x, M, H, F, f"M={M} H={H} F={F}")
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), "one launch != two launches"
     h1, h2 = h_of(work1, M, F), h_of(work2, M, F)
@@ -135,9 +129,9 @@ def test_mlp_full_size(M):
     assert w4.mlp_one_launch(M, H, F) == 1, "the benchmark shape should run in one launch"
     say(f"[mlp full] M={M}")
     host, dev, x = block(300, M, H, F)
-    y, work = run(dev, x, M, H, F, mode=0)
+    y, work = run(dev, x, M, H, F, one_launch=True)
     check(y, host, x, M, H, F, f"full M={M}")
-    y2, _ = run(dev, x, M, H, F, mode=1)
+    y2, _ = run(dev, x, M, H, F, one_launch=False)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
     assert counters_zero(work)
 
@@ -149,20 +143,15 @@ def test_barrier_timeout_is_flagged_and_recovers():
     dx = d_bf16(x)
     work = w4.new_workspace_mlp(M, H, F, "cuda")
     say("[mlp timeout] poll limit 0")
-    w4.mlp_set_options(0, 0)          # every workgroup but the last to arrive gives up at once
-    try:
-        w4.mlp_swiglu(*dev, dx, workspace=work)
-        torch.cuda.synchronize()
-    finally:
-        w4.mlp_set_options(0, 1 << 20)
-    flag = work[w4.MLP_TIMEOUT_OFFSET:w4.MLP_TIMEOUT_OFFSET + 4].view(torch.int32).item()
-    assert flag == 1
+    # every workgroup but the last to arrive gives up at once
+    w4.mlp_swiglu(*dev, dx, workspace=work, one_launch=True, spin_limit=0)
+    assert w4.mlp_timed_out(work)
     work[w4.MLP_TIMEOUT_OFFSET:w4.MLP_TIMEOUT_OFFSET + 4] = 0
     assert counters_zero(work), "counters must be reset even after a time-out"
-    y = w4.mlp_swiglu(*dev, dx, workspace=work)
+    y = w4.mlp_swiglu(*dev, dx, workspace=work, one_launch=True)
     torch.cuda.synchronize()
     check(y, host, x, M, H, F, "after time-out")
-    assert work[w4.MLP_TIMEOUT_OFFSET:w4.MLP_TIMEOUT_OFFSET + 4].view(torch.int32).item() == 0
+    assert not w4.mlp_timed_out(work)
 
 
 def test_workspace_reused_across_shapes():
@@ -170,37 +159,30 @@ def test_workspace_reused_across_shapes():
     work = w4.new_workspace_mlp(8, H, F, "cuda")     # the largest of the calls below
     for M in (8, 1, 3, 8, 5):
         host, dev, x = block(500, M, H, F)
-        y, _ = run(dev, x, M, H, F, mode=0, work=work)
+        y, _ = run(dev, x, M, H, F, one_launch=True, work=work)
         check(y, host, x, M, H, F, f"reuse M={M}")
         assert counters_zero(work)
 
 
-@pytest.mark.parametrize("mode", [0, 2])
-def test_graph_capture_replays_match_eager(mode):
-    """Mode 0 captures two launches, mode 2 the one-launch persistent kernel;
-    both must replay to the eager (one-launch) result, bit for bit."""
-    w4.mlp_set_options(mode, 1 << 20)
-    try:
-        _graph_replays_match_eager()
-    finally:
-        w4.mlp_set_options(0, 1 << 20)
-
-
-def _graph_replays_match_eager():
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_graph_capture_replays_match_eager(one_launch):
+    """Captured calls take two launches (a cooperative launch is not captured),
+    whatever the option; the replays must equal the eager result (one launch
+    when asked for), bit for bit."""
     for M, H, F in [(1, 5120, 17408), (7, 5120, 17408)]:
         host, dev, x = block(600, M, H, F)
         dx = d_bf16(x)
         work = w4.new_workspace_mlp(M, H, F, "cuda")
-        eager = w4.mlp_swiglu(*dev, dx, workspace=work).clone()
+        eager = w4.mlp_swiglu(*dev, dx, workspace=work, one_launch=one_launch).clone()
         y = torch.empty_like(eager)
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            w4.mlp_swiglu(*dev, dx, y=y, workspace=work)
+            w4.mlp_swiglu(*dev, dx, y=y, workspace=work, one_launch=one_launch)
         torch.cuda.current_stream().wait_stream(s)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            w4.mlp_swiglu(*dev, dx, y=y, workspace=work)
+            w4.mlp_swiglu(*dev, dx, y=y, workspace=work, one_launch=one_launch)
         for _ in range(3):
             y.zero_()
             graph.replay()
