@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["gemm", "gemm_gate_up_swiglu", "gemm_argmax", "dequant", "quantize", "workspace_size",
+__all__ = ["gemm", "gemm_noalloc", "gemm_gate_up_swiglu", "gemm_argmax", "dequant", "quantize", "workspace_size",
            "workspace_size_argmax",
            "workspace_size_gate_up", "new_workspace", "W4A16Error", "library_path", "lib", "MAX_M"]
 
@@ -53,6 +53,8 @@ def lib():
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     L.w4a16_gemm.argtypes = [P, P, P, P, P, I, I, I, P, Z, P]
     L.w4a16_gemm.restype = I
+    L.w4a16_gemm_noalloc.argtypes = [P, P, P, P, P, I, I, I, P]
+    L.w4a16_gemm_noalloc.restype = I
     L.w4a16_gemm_gate_up_swiglu.argtypes = [P, P, P, P, P, P, P, P, I, I, I, P, Z, P]
     L.w4a16_gemm_gate_up_swiglu.restype = I
     L.w4a16_dequant.argtypes = [P, P, P, P, I, I, P]
@@ -172,6 +174,30 @@ def gemm(wq, ws, g, x, y=None, workspace=None, stream=None):
                           _ptr(workspace), wbytes, _stream(stream))
     if st != OK:
         raise W4A16Error(st, "w4a16_gemm")
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # W4A16_NOALLOC_SCRATCH_BYTES
+
+
+def gemm_noalloc(wq, ws, g, x, y=None, stream=None):
+    """gemm without a workspace: the library's own static device scratch holds
+    the split-K partials (for callers that cannot allocate).  y must be given
+    by such a caller; calls that overlap in time on one GPU race."""
+    N, K = _weights(wq, ws, g, "")
+    _check(x, "x", torch.bfloat16, 2)
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError(f"x has K={x.shape[1]}, weights have K={K}")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(y, "y", torch.bfloat16, 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y must be ({M}, {N})")
+    st = lib().w4a16_gemm_noalloc(_ptr(wq), _ptr(ws), _ptr(g), _ptr(x), _ptr(y), M, N, K,
+                                  _stream(stream))
+    if st != OK:
+        raise W4A16Error(st, "w4a16_gemm_noalloc")
     return y
 
 

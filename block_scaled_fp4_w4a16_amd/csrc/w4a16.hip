@@ -490,6 +490,42 @@ w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 
+// ---- no-allocation variant of w4a16_gemm --------------------------------------
+// The split-K scratch (arrival counters, then fp32 partials) in a file-scope
+// device array: one copy per GPU, at a per-device address.  Host code never
+// passes `scratch` itself to a kernel (in host code that name is only a
+// stand-in for the symbol); it passes the address hipGetSymbolAddress returns
+// for the current device, kept in g_scratch.
+constexpr size_t kNoallocScratchBytes = W4A16_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoallocScratchBytes % 256 == 0 && kNoallocScratchBytes > kCounterBytes, "scratch size");
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device; nullptr until set up
+
+__global__ void __launch_bounds__(256) k_zero_words(int* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+// Once per device, with that device current: the array's device address, and
+// a clear of its arrival counters enqueued on `stream` (a kernel, so that a
+// call being captured into a graph records no memset node).
+w4a16_status_t noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return W4A16_ERR_LAUNCH;
+  void* p = __atomic_load_n(&g_scratch[dev], __ATOMIC_ACQUIRE);
+  if (p == nullptr) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr)
+      return W4A16_ERR_LAUNCH;
+    hipLaunchKernelGGL(k_zero_words, dim3(1), dim3(256), 0, stream, static_cast<int*>(q),
+                       (int)(kCounterBytes / sizeof(int)));
+    if (hipGetLastError() != hipSuccess) return W4A16_ERR_LAUNCH;
+    __atomic_store_n(&g_scratch[dev], q, __ATOMIC_RELEASE);
+    p = q;
+  }
+  *out = p;
+  return W4A16_OK;
+}
+
 }  // namespace
 }  // namespace w4a16
 
@@ -529,6 +565,35 @@ w4a16_status_t w4a16_gemm(const uint8_t* wq, const uint8_t* ws, const float* g,
   a.N = N;
   a.K = K;
   return run_matmul(a, kEpiPlain, workspace, workspace_bytes, stream);
+}
+
+w4a16_status_t w4a16_gemm_noalloc(const uint8_t* wq, const uint8_t* ws, const float* g,
+                                  const uint16_t* x, uint16_t* y, int M, int N, int K,
+                                  hipStream_t stream) {
+  if (!wq || !ws || !g || !x || !y) return W4A16_ERR_INVALID_VALUE;
+  w4a16_status_t st = check_shape(M, N, K);
+  if (st != W4A16_OK) return st;
+  if (!aligned(wq, 16) || !aligned(ws, 16) || !aligned(x, 16) || !aligned(g, 4) ||
+      !aligned(y, 4))
+    return W4A16_ERR_UNSUPPORTED;
+  const Plan pl = plan_gemm(M, N, K, kEpiPlain);
+  if (pl.S == 0 || pl.lds > kMaxLds || pl.ws > kNoallocScratchBytes) return W4A16_ERR_UNSUPPORTED;
+  void* work = nullptr;
+  st = noalloc_scratch(stream, &work);
+  if (st != W4A16_OK) return st;
+  MatArgs a{};
+  a.wq0 = wq;
+  a.ws0 = ws;
+  a.g0 = g;
+  a.wq1 = wq;
+  a.ws1 = ws;
+  a.g1 = g;
+  a.x = x;
+  a.y = y;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return run_matmul(a, kEpiPlain, work, kNoallocScratchBytes, stream);
 }
 
 w4a16_status_t w4a16_gemm_gate_up_swiglu(const uint8_t* wq_gate, const uint8_t* ws_gate,

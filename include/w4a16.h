@@ -89,6 +89,27 @@ w4a16_status_t w4a16_gemm(const uint8_t* wq, const uint8_t* ws, const float* g,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * w4a16_gemm for callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation, kernels and results as w4a16_gemm, without a workspace
+ * argument.  Its split-K scratch is a library-owned static device array of
+ * W4A16_NOALLOC_SCRATCH_BYTES bytes on each GPU the library runs on, held
+ * until the process ends; the call allocates nothing.  Shapes whose
+ * w4a16_workspace_size exceeds that array are rejected with
+ * W4A16_ERR_UNSUPPORTED (every benchmark shape up to M = 32 fits).  The first
+ * call on a device looks the array up and enqueues a clear of its arrival
+ * counters on `stream`; every call leaves them zero.  All calls on one GPU
+ * share the array: calls that overlap in time on one GPU (different streams
+ * or threads) race and their results are undefined; calls made one after
+ * another, on any streams, are fine.  Errors as w4a16_gemm; W4A16_ERR_LAUNCH
+ * also reports a failed lookup of the array.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (16u << 20)
+w4a16_status_t w4a16_gemm_noalloc(const uint8_t* wq, const uint8_t* ws, const float* g,
+                                  const uint16_t* x, uint16_t* y, int M, int N, int K,
+                                  hipStream_t stream);
+
+/*
  * Fused MLP input projections with SwiGLU:
  *   a = x * Wg^T,  b = x * Wu^T  (both fp32, each with its own g),
  *   y[M][N] = bf16( silu(a) * b ),  silu(a) = a / (1 + exp(-a)).

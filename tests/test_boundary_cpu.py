@@ -61,6 +61,28 @@ def call_fused(lib, wq=P, ws=P, g=P, x=P, y=P, M=1, N=64, K=256, work=0, wbytes=
     return lib.w4a16_gemm_gate_up_swiglu(wq, ws, g, wq, ws, g, x, y, M, N, K, work, wbytes, None)
 
 
+def call_noalloc(lib, wq=P, ws=P, g=P, x=P, y=P, M=1, N=64, K=256, work=0, wbytes=0):
+    return lib.w4a16_gemm_noalloc(wq, ws, g, x, y, M, N, K, None)
+
+
+def test_noalloc_rejects_bad_calls_and_oversize_shapes(lib):
+    for arg in ("wq", "ws", "g", "x", "y"):
+        assert call_noalloc(lib, **{arg: 0}) == w4.ERR_INVALID_VALUE, arg
+    assert call_noalloc(lib, M=0) == w4.ERR_INVALID_VALUE
+    assert call_noalloc(lib, M=33) == w4.ERR_UNSUPPORTED
+    assert call_noalloc(lib, K=272) == w4.ERR_UNSUPPORTED
+    assert call_noalloc(lib, x=P + 8) == w4.ERR_UNSUPPORTED
+    # the head at M = 32 needs more split-K scratch than the static array holds
+    assert w4.workspace_size(32, 248320, 5120) > w4.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(lib, M=32, N=248320, K=5120) == w4.ERR_UNSUPPORTED
+    hdr = open(HEADER).read()
+    assert re.search(r"#define W4A16_NOALLOC_SCRATCH_BYTES \(16u << 20\)", hdr)
+    assert w4.NOALLOC_SCRATCH_BYTES == 16 << 20
+    # every benchmark shape up to M = 32 fits
+    for M, N, K in ((32, 5120, 17408), (32, 17408, 5120), (32, 5120, 5120)):
+        assert w4.workspace_size(M, N, K) <= w4.NOALLOC_SCRATCH_BYTES
+
+
 @pytest.mark.parametrize("call", [call_gemm, call_fused])
 def test_null_pointers_rejected(lib, call):
     for arg in ("wq", "ws", "g", "x", "y"):
