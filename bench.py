@@ -3,26 +3,29 @@
 Default workload (one JSON line on stdout): the square projection, K = N =
 5120, M = 1, with 64 byte-identical NVFP4 weight copies (943.7 MB, past the
 256 MB Infinity Cache) cycled call after call.  One step = one pass over the
-64 copies (64 calls).  Metric: effective weight GB/s = (N*K/2 codes + N*K/16
-scales + 4 B g) per call / time per call, plus % of the 8 TB/s HBM peak.
-The same line also reports the same workload at M = 7 (a speculative-verify
-block) under "square_M7"; `value` is the M = 1 figure.
+64 copies (64 calls), captured once in a HIP graph and replayed.  Metric:
+effective weight GB/s = (N*K/2 codes + N*K/16 scales + 4 B g) per call / time
+per call, with % of the 8 TB/s HBM peak.  Exactly --steps replays are timed
+(HIP events on the replay stream, split into 5 windows whose median and
+minimum are also reported), after --warmup untimed replays.
 
-`--extra` also times the fused gate/up (M = 1, 7) and down (M = 1, 2, 4, 7,
-8) configurations and the whole MLP block (gate/up + SwiGLU + down, one
-persistent launch vs two launches, M = 1, 7), and `--tower` the full-tower
-decode sweep (64 layers of the MLP block and q/k/v/o plus the 248320-wide
-head, one HIP graph replay per token, M = 1 and 7); both report under "extra"
-in the same line.
+The same line carries the metric's two operating points (M = 1 decode and
+M = 7, a verify block of 6 drafts + 1) on the configurations that define
+them: the square projection at M = 7, the fused gate/up + SwiGLU (K = 5120,
+2 x N = 17408, 32 layer copies) and the down projection (K = 17408,
+N = 5120, 32 copies), each at M = 1 and 7 with median and minimum over 5
+timed windows; the oracle timed on the host (one thread and all cores); and
+an achievable-read calibration.  `--extra` adds the down projection at
+M = 2, 4, 8, 16, 32 and the MLP block; `--tower` the full-tower decode sweep.
 
-The timed region brackets the calls with HIP events recorded on the stream
-the kernels run on; inputs are resident in HBM before timing starts.
+Inputs are resident in HBM before any timed region starts.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -35,6 +38,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic_square_m1.json")
+WINDOWS = 5
 
 
 def kernel_source_hash():
@@ -87,29 +91,99 @@ def replicate(t, copies):
     return [t.clone() for _ in range(copies)]
 
 
-def time_calls(fns, cycles, warmup_cycles, stream):
-    """Run every fn in `fns` once per cycle; return seconds per call (events)."""
+def gpu_weights(seed, N, K, dev):
+    """W ~ N(0, 0.02) fp32 drawn on the device from a seeded generator and
+    NVFP4-encoded by the library's quantiser (w4a16_quantize, bit-exact to the
+    oracle's recipe): (wq, ws, g) device tensors.  Used for the large
+    configurations, whose host-side encoding would take tens of seconds;
+    the bytes differ from synth's, the distribution and recipe do not."""
     import torch
-    for _ in range(warmup_cycles):
-        for f in fns:
-            f()
+    import block_scaled_fp4_w4a16_amd as w4
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    w = torch.randn((N, K), generator=gen, device=dev, dtype=torch.float32).mul_(0.02)
+    wq, ws, g = w4.quantize(w)
+    del w
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(cycles):
-        for f in fns:
-            f()
-    end.record(stream)
-    end.synchronize()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3 / (cycles * len(fns))
+    return wq, ws, g
 
 
-def bench_square(args, dev, stream):
-    """Square GEMV: one step = one call per weight copy (64 calls), captured
-    once in a HIP graph and replayed; also times the same calls launched
-    eagerly from Python for reference."""
+def capture(fns, stream):
+    """A HIP graph holding one call of each fn(stream) (after one eager warm
+    call of each on the capture stream)."""
+    import torch
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        for f in fns:
+            f(cap)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for f in fns:
+            f(cap)
+    torch.cuda.synchronize()
+    return graph
+
+
+def timed_replays(graph, stream, steps, windows=WINDOWS):
+    """Replay `graph` exactly `steps` times on `stream`, bracketed by device
+    synchronisation; HIP events split the replays into `windows` windows.
+    Returns (total seconds, [seconds per replay of each window])."""
+    import torch
+    windows = max(1, min(windows, steps))
+    bounds = [round(i * steps / windows) for i in range(windows + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(windows + 1)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        for w in range(windows):
+            for _ in range(bounds[w + 1] - bounds[w]):
+                graph.replay()
+            ev[w + 1].record(stream)
+    ev[-1].synchronize()
+    torch.cuda.synchronize()
+    total = ev[0].elapsed_time(ev[-1]) * 1e-3
+    per = [ev[w].elapsed_time(ev[w + 1]) * 1e-3 / (bounds[w + 1] - bounds[w]) for w in range(windows)]
+    return total, per
+
+
+def warm(graph, stream, seconds=0.05):
+    """Untimed replays for at least `seconds`, so that the configuration timed
+    next runs at steady clocks."""
+    import torch
+    t0 = time.perf_counter()
+    while True:
+        with torch.cuda.stream(stream):
+            graph.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+
+
+def config_line(calls_per_replay, bytes_per_call, per_window, replays_per_window):
+    """µs per call, GB/s and fraction of peak from the median window, and the
+    fastest window."""
+    us = [p / calls_per_replay * 1e6 for p in per_window]
+    med, mn = statistics.median(us), min(us)
+    gbs = bytes_per_call / (med * 1e-6) / 1e9
+    return {"us_per_call": round(med, 3), "us_per_call_min": round(mn, 3), "gbs": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "windows": len(us),
+            "calls_timed": calls_per_replay * replays_per_window * len(us)}
+
+
+def time_config(fns, stream, bytes_per_call, replays_per_window=2):
+    graph = capture(fns, stream)
+    warm(graph, stream)
+    _, per = timed_replays(graph, stream, replays_per_window * WINDOWS)
+    del graph
+    return config_line(len(fns), bytes_per_call, per, replays_per_window)
+
+
+# ---- the default workload: square projection, M = 1 ------------------------------
+
+def square_setup(dev):
     import torch
     import block_scaled_fp4_w4a16_amd as w4
     import synth
@@ -123,208 +197,161 @@ def bench_square(args, dev, stream):
     gs = replicate(torch.tensor([g], dtype=torch.float32, device=dev), copies)
     y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
     work = w4.new_workspace(1, N, K, dev)   # zeroed once; every call leaves it zeroed
-    bpc = weight_bytes(N, K)
+    return dict(N=N, K=K, copies=copies, wqs=wqs, wss=wss, gs=gs, x=x, y=y, work=work, seed_x=c["seed_x"])
 
-    def step(strm):
-        for i in range(copies):
-            w4.gemm(wqs[i], wss[i], gs[i], x, y=y, workspace=work, stream=strm)
 
-    # eager reference (Python launches each call)
-    step(stream)
-    torch.cuda.synchronize()
-    t_eager = time_calls([lambda: step(stream)], 3, 1, stream) / copies
+def square_fns(sq, x, y, work):
+    import block_scaled_fp4_w4a16_amd as w4
+    return [lambda s, i=i: w4.gemm(sq["wqs"][i], sq["wss"][i], sq["gs"][i], x, y=y, workspace=work, stream=s)
+            for i in range(sq["copies"])]
 
-    # capture one step, replay `warmup` untimed and exactly `steps` timed
-    graph = torch.cuda.CUDAGraph()
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        step(cap)
-    stream.wait_stream(cap)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(graph, stream=cap):
-        step(cap)
-    torch.cuda.synchronize()
+
+def bench_square(args, dev, stream, sq):
+    """One step = the 64 calls, captured once in a HIP graph; `warmup`
+    untimed replays, then exactly `steps` timed replays."""
+    import torch
+    graph = capture(square_fns(sq, sq["x"], sq["y"], sq["work"]), stream)
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             graph.replay()
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        end.record(stream)
-    end.synchronize()
-    torch.cuda.synchronize()
+    total, per = timed_replays(graph, stream, args.steps)
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end)
-    calls = args.steps * copies
-    per_call = ms * 1e-3 / calls
-    # the same calls for a speculative-verify block (M = 7: K_spec = 6 drafts
-    # + 1), each weight read once for all rows; timed like the extra configs
-    M7 = 7
-    x7 = to_dev_bf16(synth.activations(c["seed_x"], M7, K), dev)
-    y7 = torch.empty((M7, N), dtype=torch.bfloat16, device=dev)
-    work7 = w4.new_workspace(M7, N, K, dev)
-    t7 = graph_time([lambda s, i=i: w4.gemm(wqs[i], wss[i], gs[i], x7, y=y7, workspace=work7, stream=s)
-                     for i in range(copies)], 10, stream)
-    return dict(N=N, K=K, copies=copies, calls=calls, ms=ms, wall=wall, per_call=per_call,
-                bytes_per_call=bpc, gbs=bpc / per_call / 1e9, eager_per_call=t_eager,
-                eager_gbs=bpc / t_eager / 1e9, m7_per_call=t7, m7_gbs=bpc / t7 / 1e9)
+    del graph
+    calls = args.steps * sq["copies"]
+    return dict(total=total, wall=wall, per_window=per, calls=calls, per_call=total / calls)
 
 
-def graph_time(fns, cycles, stream):
-    """Seconds per call of fns, captured once in a HIP graph (one call each)
-    and replayed `cycles` times after at least 50 ms of untimed replays."""
-    import torch
-    cap = torch.cuda.Stream()
-    cap.wait_stream(stream)
-    with torch.cuda.stream(cap):
-        for f in fns:
-            f(cap)
-    stream.wait_stream(cap)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=cap):
-        for f in fns:
-            f(cap)
-    torch.cuda.synchronize()
-    # untimed replays for at least 50 ms, so that the first configuration timed
-    # after the host-side weight generation runs at steady clocks
-    t_warm = time.perf_counter()
-    while True:
-        with torch.cuda.stream(stream):
-            graph.replay()
-        torch.cuda.synchronize()
-        if time.perf_counter() - t_warm >= 0.05:
-            break
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        start.record(stream)
-        for _ in range(cycles):
-            graph.replay()
-        end.record(stream)
-    end.synchronize()
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e-3 / (cycles * len(fns))
+def profile_square(args, dev, stream):
+    """Only the default workload's graph replays (for a rocprofv3 kernel
+    trace whose dispatches are exactly the timed calls and their warm-up)."""
+    sq = square_setup(dev)
+    r = bench_square(args, dev, stream, sq)
+    bpc = weight_bytes(sq["N"], sq["K"])
+    print(json.dumps({"mode": "profile-square", "steps": args.steps, "warmup": args.warmup,
+                      "calls_timed": r["calls"], "us_per_call": round(r["per_call"] * 1e6, 4),
+                      "gbs": round(bpc / r["per_call"] / 1e9, 1)}), flush=True)
 
 
-def bench_extra(dev, stream, cycles=10):
+# ---- the metric's configurations ------------------------------------------------
+
+def bench_configs(dev, stream, sq, extra=False):
+    """Square M = 7; gate/up + SwiGLU M = 1, 7; down M = 1, 7 (with --extra
+    also down M = 2, 4, 8, 16, 32 and the MLP block)."""
     import torch
     import block_scaled_fp4_w4a16_amd as w4
     import synth
     out = {}
+    bsq = weight_bytes(sq["N"], sq["K"])
+    x7 = to_dev_bf16(synth.activations(sq["seed_x"], 7, sq["K"]), dev)
+    y7 = torch.empty((7, sq["N"]), dtype=torch.bfloat16, device=dev)
+    out["square_M7"] = time_config(square_fns(sq, x7, y7, w4.new_workspace(7, sq["N"], sq["K"], dev)), stream,
+                                   bsq, replays_per_window=2)
+    log(f"[bench] square M=7: {out['square_M7']['us_per_call']} us/call, {out['square_M7']['gbs']} GB/s")
+
     c = synth.CONFIGS["gate_up"]
     N, K, copies = c["N"], c["K"], c["copies"]
-    log(f"[bench] generating gate_up K={K} N={N} x{copies}")
-    wg = synth.nvfp4_weights(c["seed_gate"], N, K)
-    wu = synth.nvfp4_weights(c["seed_up"], N, K)
-    G = [replicate(to_dev_u8(wg[0], dev), copies), replicate(to_dev_u8(wg[1], dev), copies),
-         replicate(torch.tensor([wg[2]], device=dev), copies)]
-    U = [replicate(to_dev_u8(wu[0], dev), copies), replicate(to_dev_u8(wu[1], dev), copies),
-         replicate(torch.tensor([wu[2]], device=dev), copies)]
-    for M in c["Ms"]:
+    log(f"[bench] generating gate/up K={K} 2 x N={N} x{copies} (device quantiser)")
+    G = gpu_weights(c["seed_gate"], N, K, dev)
+    U = gpu_weights(c["seed_up"], N, K, dev)
+    Gs = [replicate(t, copies) for t in G]
+    Us = [replicate(t, copies) for t in U]
+    del G, U
+    b_gu = 2 * weight_bytes(N, K)
+    for M in (1, 7):
         x = to_dev_bf16(synth.activations(c["seed_x"], M, K), dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         work = w4.new_workspace(M, N, K, dev, fused=True)
-        fns = [lambda s, i=i: w4.gemm_gate_up_swiglu(G[0][i], G[1][i], G[2][i], U[0][i], U[1][i],
-                                                     U[2][i], x, y=y, workspace=work, stream=s)
-               for i in range(copies)]
-        t = graph_time(fns, cycles, stream)
-        b = 2 * weight_bytes(N, K)
-        out[f"gate_up_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
-        log(f"[bench] gate_up M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
+        fns = [lambda s, i=i: w4.gemm_gate_up_swiglu(Gs[0][i], Gs[1][i], Gs[2][i], Us[0][i], Us[1][i], Us[2][i],
+                                                     x, y=y, workspace=work, stream=s) for i in range(copies)]
+        out[f"gate_up_M{M}"] = time_config(fns, stream, b_gu)
+        log(f"[bench] gate/up M={M}: {out[f'gate_up_M{M}']['us_per_call']} us/call, {out[f'gate_up_M{M}']['gbs']} GB/s")
+
     c = synth.CONFIGS["down"]
     N, K, copies = c["N"], c["K"], c["copies"]
-    log(f"[bench] generating down K={K} N={N} x{copies}")
-    wd = synth.nvfp4_weights(c["seed_w"], N, K)
-    D = [replicate(to_dev_u8(wd[0], dev), copies), replicate(to_dev_u8(wd[1], dev), copies),
-         replicate(torch.tensor([wd[2]], device=dev), copies)]
-    for M in c["Ms"]:
+    log(f"[bench] generating down K={K} N={N} x{copies} (device quantiser)")
+    D = gpu_weights(c["seed_w"], N, K, dev)
+    Ds = [replicate(t, copies) for t in D]
+    del D
+    b_d = weight_bytes(N, K)
+    for M in ((1, 2, 4, 7, 8, 16, 32) if extra else (1, 7)):
         x = to_dev_bf16(synth.swiglu_activations(c["seed_a"], c["seed_b"], M, K), dev)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         work = w4.new_workspace(M, N, K, dev)
-        fns = [lambda s, i=i: w4.gemm(D[0][i], D[1][i], D[2][i], x, y=y, workspace=work, stream=s)
+        fns = [lambda s, i=i: w4.gemm(Ds[0][i], Ds[1][i], Ds[2][i], x, y=y, workspace=work, stream=s)
                for i in range(copies)]
-        t = graph_time(fns, cycles, stream)
-        b = weight_bytes(N, K)
-        out[f"down_M{M}"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
-        log(f"[bench] down M={M}: {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
-    # the whole MLP block (gate/up + SwiGLU + down) per call: one persistent
-    # launch (forced under capture), and the same calls in two launches (what
-    # a captured call takes by default)
-    H, F = N, K          # the down projection's output and input widths
-    nb = min(len(G[0]), len(D[0]))
-    for M in (1, 7):
-        x = to_dev_bf16(synth.activations(synth.CONFIGS["gate_up"]["seed_x"], M, H), dev)
-        y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
-        work = w4.new_workspace_mlp(M, H, F, dev)
-        fns = [lambda s, i=i: w4.mlp_swiglu((G[0][i], G[1][i], G[2][i]), (U[0][i], U[1][i], U[2][i]),
-                                            (D[0][i], D[1][i], D[2][i]), x, y=y, workspace=work, stream=s)
-               for i in range(nb)]
+        out[f"down_M{M}"] = time_config(fns, stream, b_d)
+        log(f"[bench] down M={M}: {out[f'down_M{M}']['us_per_call']} us/call, {out[f'down_M{M}']['gbs']} GB/s")
+
+    if extra:
+        # the whole MLP block per call: two launches (graph replay), and eager
+        # calls with one (cooperative) launch and with two
+        H, F = N, K
         b = 2 * weight_bytes(F, H) + weight_bytes(H, F)
-        # captured calls take two launches; the one-launch (cooperative) path
-        # runs only for eager calls, so both are also timed eagerly
-        res = {"one_launch_possible": w4.mlp_one_launch(M, H, F)}
-        t = graph_time(fns, cycles, stream)
-        res["two_launches_graph"] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9,
-                                         pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
-        log(f"[bench] mlp block M={M} (two launches, graph): {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
-        for one, name in ((True, "one_launch_eager"), (False, "two_launches_eager")):
-            efns = [lambda i=i: w4.mlp_swiglu((G[0][i], G[1][i], G[2][i]), (U[0][i], U[1][i], U[2][i]),
-                                              (D[0][i], D[1][i], D[2][i]), x, y=y, workspace=work,
-                                              stream=stream, one_launch=one)
-                    for i in range(nb)]
-            t = time_calls(efns, cycles, 2, stream)
-            res[name] = dict(us_per_call=t * 1e6, gbs=b / t / 1e9, pct_peak=100 * b / t / 1e9 / HBM_PEAK_GBS)
-            log(f"[bench] mlp block M={M} ({name}): {t*1e6:.2f} us/call, {b/t/1e9:.0f} GB/s")
-        out[f"mlp_M{M}"] = res
-    del G, U, D
+        for M in (1, 7):
+            x = to_dev_bf16(synth.activations(synth.CONFIGS["gate_up"]["seed_x"], M, H), dev)
+            y = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+            work = w4.new_workspace_mlp(M, H, F, dev)
+
+            def call(s, i, one):
+                w4.mlp_swiglu((Gs[0][i], Gs[1][i], Gs[2][i]), (Us[0][i], Us[1][i], Us[2][i]),
+                              (Ds[0][i], Ds[1][i], Ds[2][i]), x, y=y, workspace=work, stream=s, one_launch=one)
+            res = {"one_launch_possible": w4.mlp_one_launch(M, H, F)}
+            res["two_launches_graph"] = time_config([lambda s, i=i: call(s, i, False) for i in range(copies)],
+                                                    stream, b)
+            for one, name in ((True, "one_launch_eager"), (False, "two_launches_eager")):
+                for i in range(copies):
+                    call(stream, i, one)
+                torch.cuda.synchronize()
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record(stream)
+                for _ in range(4):
+                    for i in range(copies):
+                        call(stream, i, one)
+                ev1.record(stream)
+                ev1.synchronize()
+                t = ev0.elapsed_time(ev1) * 1e-3 / (4 * copies)
+                res[name] = {"us_per_call": round(t * 1e6, 3), "gbs": round(b / t / 1e9, 1)}
+            out[f"mlp_M{M}"] = res
+            log(f"[bench] mlp block M={M}: {json.dumps(res)}")
+    del Gs, Us, Ds
+    torch.cuda.empty_cache()
     return out
 
 
 def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
     """Full-tower decode sweep, one token = one HIP graph replay of
     `layers` x (the MLP block: gate/up + SwiGLU 5120 -> 2 x 17408 and down
-    17408 -> 5120 through w4a16_mlp_swiglu, which takes two launches under
-    capture; q, k, v, o 5120 -> 5120) followed by the 5120 -> 248320 head GEMV
-    with fused greedy argmax (the head alone is also timed with and without
-    it): 385 launches and 14.1 GB of distinct weight allocations per token.
-    The MLP
-    chain is wired (SwiGLU output feeds down, down's output feeds the next
-    layer's gate/up); q/k/v/o and the head read fixed synthetic activations
-    (there is no attention).  Weights per layer are byte-identical replicas of
-    one encoded matrix per kind; the head matrix tiles the rows of the square
-    matrix (48.5 copies of its 5120 rows), since HBM traffic depends on the
-    addresses read, not on the values."""
+    17408 -> 5120, two launches; q, k, v, o 5120 -> 5120) followed by the
+    5120 -> 248320 head GEMV with fused greedy argmax (the head alone is also
+    timed with and without it): 385 launches and 14.1 GB of distinct weight
+    allocations per token.  The MLP chain is wired (SwiGLU output feeds down,
+    down's output feeds the next layer's gate/up); q/k/v/o and the head read
+    fixed synthetic activations (there is no attention).  Weights per layer
+    are byte-identical replicas of one encoded matrix per kind; the head
+    matrix tiles the rows of the square matrix, since HBM traffic depends on
+    the addresses read, not on the values."""
     import torch
     import block_scaled_fp4_w4a16_amd as w4
     import synth
     H, F, V = 5120, 17408, 248320
     cg, cd, cs = synth.CONFIGS["gate_up"], synth.CONFIGS["down"], synth.CONFIGS["square"]
     log(f"[bench] tower: encoding gate/up/down/square, {layers} layers + head")
-    enc = {
-        "gate": synth.nvfp4_weights(cg["seed_gate"], F, H),
-        "up": synth.nvfp4_weights(cg["seed_up"], F, H),
-        "down": synth.nvfp4_weights(cd["seed_w"], H, F),
-        "sq": synth.nvfp4_weights(cs["seed_w"], H, H),
-    }
-    dev_enc = {k: (to_dev_u8(v[0], dev), to_dev_u8(v[1], dev),
-                   torch.tensor([v[2]], dtype=torch.float32, device=dev)) for k, v in enc.items()}
+    enc = {"gate": gpu_weights(cg["seed_gate"], F, H, dev), "up": gpu_weights(cg["seed_up"], F, H, dev),
+           "down": gpu_weights(cd["seed_w"], H, F, dev)}
+    sq = synth.nvfp4_weights(cs["seed_w"], H, H)
+    enc["sq"] = (to_dev_u8(sq[0], dev), to_dev_u8(sq[1], dev),
+                 torch.tensor([sq[2]], dtype=torch.float32, device=dev))
 
     def copies(kind, n):
-        return [tuple(t.clone() for t in dev_enc[kind]) for _ in range(n)]
+        return [tuple(t.clone() for t in enc[kind]) for _ in range(n)]
     L = {"gate": copies("gate", layers), "up": copies("up", layers), "down": copies("down", layers),
          "q": copies("sq", layers), "k": copies("sq", layers), "v": copies("sq", layers),
          "o": copies("sq", layers)}
     reps = (V + H - 1) // H
-    head = (torch.cat([dev_enc["sq"][0]] * reps)[:V].contiguous(),
-            torch.cat([dev_enc["sq"][1]] * reps)[:V].contiguous(), dev_enc["sq"][2].clone())
-    del dev_enc
+    head = (torch.cat([enc["sq"][0]] * reps)[:V].contiguous(),
+            torch.cat([enc["sq"][1]] * reps)[:V].contiguous(), enc["sq"][2].clone())
+    del enc
     b_layer = 2 * weight_bytes(F, H) + weight_bytes(H, F) + 4 * weight_bytes(H, H)
     b_token = layers * b_layer + weight_bytes(V, H)
     out = {}
@@ -350,28 +377,34 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
                     q = L[kind][i]
                     w4.gemm(q[0], q[1], q[2], xa, y=ya, workspace=wk_sq, stream=s)
                 x = nx
-            # greedy decoding: the head's argmax, without materialising logits
-            w4.gemm_argmax(head[0], head[1], head[2], x, idx=tok_idx, val=tok_val, workspace=wk_hd,
-                           stream=s)
+            w4.gemm_argmax(head[0], head[1], head[2], x, idx=tok_idx, val=tok_val, workspace=wk_hd, stream=s)
 
-        t = graph_time([token], replays, stream)
-        t_head = graph_time([lambda s: w4.gemm(head[0], head[1], head[2], x0, y=logits, workspace=wk_hd0,
-                                               stream=s)] * 8, replays, stream)
-        t_head_am = graph_time([lambda s: w4.gemm_argmax(head[0], head[1], head[2], x0, idx=tok_idx, val=tok_val,
-                                                         workspace=wk_hd, stream=s)] * 8, replays, stream)
+        g = capture([token], stream)
+        warm(g, stream)
+        _, per = timed_replays(g, stream, replays)
+        t = statistics.median(per)
+        del g
+        gh = capture([lambda s: w4.gemm(head[0], head[1], head[2], x0, y=logits, workspace=wk_hd0, stream=s)] * 8,
+                     stream)
+        warm(gh, stream)
+        _, ph = timed_replays(gh, stream, replays)
+        t_head = statistics.median(ph) / 8
+        del gh
+        ga = capture([lambda s: w4.gemm_argmax(head[0], head[1], head[2], x0, idx=tok_idx, val=tok_val,
+                                               workspace=wk_hd, stream=s)] * 8, stream)
+        warm(ga, stream)
+        _, pa = timed_replays(ga, stream, replays)
+        t_am = statistics.median(pa) / 8
+        del ga
         bh = weight_bytes(V, H)
-        out[f"head_M{M}"] = dict(us_per_call=t_head * 1e6, gbs=bh / t_head / 1e9,
-                                 argmax_us_per_call=t_head_am * 1e6, argmax_gbs=bh / t_head_am / 1e9)
-        log(f"[bench] head 5120->{V} M={M}: logits {t_head*1e6:.1f} us ({bh/t_head/1e9:.0f} GB/s), "
-            f"fused argmax {t_head_am*1e6:.1f} us ({bh/t_head_am/1e9:.0f} GB/s)")
-        per_layer = 6  # captured MLP blocks run as two launches (gate/up, down)
-        out[f"tower_M{M}"] = dict(ms_per_token=t * 1e3, tokens_per_s=1.0 / t,
-                                  launches_per_token=per_layer * layers + 1,
-                                  head="fused greedy argmax",
-                                  bytes_per_token=b_token, gbs=b_token / t / 1e9,
-                                  pct_peak=100 * b_token / t / 1e9 / HBM_PEAK_GBS)
-        log(f"[bench] tower M={M}: {t*1e3:.3f} ms/token ({1/t:.1f} tok/s), {b_token/t/1e9:.0f} GB/s "
-            f"over {b_token/1e9:.2f} GB")
+        out[f"head_M{M}"] = dict(us_per_call=round(t_head * 1e6, 2), gbs=round(bh / t_head / 1e9, 1),
+                                 argmax_us_per_call=round(t_am * 1e6, 2), argmax_gbs=round(bh / t_am / 1e9, 1))
+        out[f"tower_M{M}"] = dict(ms_per_token=round(t * 1e3, 4), tokens_per_s=round(1.0 / t, 2),
+                                  launches_per_token=6 * layers + 1, head="fused greedy argmax",
+                                  bytes_per_token=b_token, gbs=round(b_token / t / 1e9, 1),
+                                  frac=round(b_token / t / 1e9 / HBM_PEAK_GBS, 4))
+        log(f"[bench] tower M={M}: {t*1e3:.3f} ms/token, {b_token/t/1e9:.0f} GB/s; head {t_head*1e6:.1f} us, "
+            f"with argmax {t_am*1e6:.1f} us")
     return out
 
 
@@ -379,10 +412,10 @@ def calibration(dev, stream, copies, call_bytes=5120 * 5120 // 2 + 5120 * 5120 /
     """Achievable HBM read rates, from a plain 128-bit non-temporal streaming
     read (libw4a16_calib.so, not the matmul library): once on a 4 GiB buffer
     (32 workgroups of 1024 threads per CU: the fastest launch shape of a sweep
-    on MI355X, 6.6-7.0 TB/s), and over `copies` buffers of one
-    square call's weight bytes cycled like the weight copies, with the GEMV's
-    grid (one workgroup of 512 threads per CU), in a HIP graph like the
-    benchmark.  The second rate includes the same per-call fixed costs."""
+    on MI355X), and over `copies` buffers of one square call's weight bytes
+    cycled like the weight copies, with the GEMV's grid (one workgroup of 512
+    threads per CU), in a HIP graph like the benchmark.  The second rate
+    includes the same per-call fixed costs."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "block_scaled_fp4_w4a16_amd", "libw4a16_calib.so")
@@ -403,11 +436,17 @@ def calibration(dev, stream, copies, call_bytes=5120 * 5120 // 2 + 5120 * 5120 /
 
     big_bytes = 4 << 30
     big = torch.ones(big_bytes, dtype=torch.uint8, device=dev)
-    t_big = graph_time([lambda s: read(big, big_bytes, 32 * cus, 1024, s)], 10, stream)
-    del big
+    g = capture([lambda s: read(big, big_bytes, 32 * cus, 1024, s)], stream)
+    warm(g, stream)
+    _, per = timed_replays(g, stream, 10)
+    t_big = statistics.median(per)
+    del g, big
     bufs = [torch.ones(call_bytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
-    t_call = graph_time([lambda s, i=i: read(bufs[i], call_bytes, cus, 512, s) for i in range(copies)], 10, stream)
-    del bufs
+    g = capture([lambda s, i=i: read(bufs[i], call_bytes, cus, 512, s) for i in range(copies)], stream)
+    warm(g, stream)
+    _, per = timed_replays(g, stream, 10)
+    t_call = statistics.median(per) / copies
+    del g, bufs
     return {"kind": "plain 128-bit non-temporal streaming read (libw4a16_calib.so)",
             "stream_4gib_gbs": round(big_bytes / t_big / 1e9, 1),
             "call_sized_bytes": call_bytes, "call_sized_copies": copies,
@@ -415,26 +454,56 @@ def calibration(dev, stream, copies, call_bytes=5120 * 5120 // 2 + 5120 * 5120 /
             "call_sized_gbs": round(call_bytes / t_call / 1e9, 1)}
 
 
-def cpu_baseline(seconds_target=12.0):
-    """The CPU oracle timed on a bounded sample of the square workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(window_s=3.0):
+    """The CPU oracle (fp64 C, OpenMP over output rows) timed on a bounded
+    sample of the default workload: repeated square GEMV calls (M = 1,
+    K = N = 5120, the same seeded inputs), median of 3 windows of about
+    `window_s` seconds each, at all host threads and at one thread."""
     import oracle
     import synth
     c = synth.CONFIGS["square"]
     N, K = c["N"], c["K"]
     wq, ws, g = synth.nvfp4_weights(c["seed_w"], N, K)
     x = synth.activations(c["seed_x"], 1, K)
-    threads = oracle.max_threads()
-    t0 = time.perf_counter()
-    oracle.gemm(wq, ws, g, x, 1, N, K, nthreads=threads)
-    one = time.perf_counter() - t0
-    reps = max(1, min(64, int(seconds_target / max(one, 1e-3))))
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    bpc = weight_bytes(N, K)
+
+    def measure(threads):
+        oracle.gemm(wq, ws, g, x, 1, N, K, nthreads=threads)   # warm
+        t0 = time.perf_counter()
         oracle.gemm(wq, ws, g, x, 1, N, K, nthreads=threads)
-    dt = (time.perf_counter() - t0) / reps
-    return dict(value=weight_bytes(N, K) / dt / 1e9, unit="GB/s", cores=threads, kind="oracle",
-                sample=f"{reps} calls of the square GEMV (M=1, K=N=5120) by the fp64 C oracle "
-                       f"with {threads} OpenMP threads; {dt*1e3:.1f} ms/call")
+        one = time.perf_counter() - t0
+        reps = max(1, int(window_s / max(one, 1e-4)))
+        per = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                oracle.gemm(wq, ws, g, x, 1, N, K, nthreads=threads)
+            per.append((time.perf_counter() - t0) / reps)
+        return statistics.median(per), reps
+
+    all_threads = oracle.max_threads()
+    dt_all, reps_all = measure(all_threads)
+    dt_one, reps_one = measure(1)
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return dict(value=round(bpc / dt_all / 1e9, 4), unit="GB/s", cores=all_threads, kind="oracle",
+                sample=f"square GEMV (M=1, K=N=5120) by the fp64 C oracle, median of 3 windows of "
+                       f"{reps_all} calls at {all_threads} threads ({dt_all*1e3:.2f} ms/call) and of "
+                       f"{reps_one} calls at 1 thread ({dt_one*1e3:.1f} ms/call)",
+                ms_per_call=round(dt_all * 1e3, 3),
+                single_thread={"value": round(bpc / dt_one / 1e9, 5), "unit": "GB/s",
+                               "ms_per_call": round(dt_one * 1e3, 2), "cores": 1},
+                cpu_model=cpu_model(), nproc=os.cpu_count(), affinity_cpus=affinity)
 
 
 def copy_calibration(dev, mib=256, reps=4):
@@ -451,28 +520,32 @@ def copy_calibration(dev, mib=256, reps=4):
     print(json.dumps({"copy_bytes_per_launch": n * 4, "reps": reps}), flush=True)
 
 
-def ingest_pmc(d):
-    """Calibrated HBM traffic of the square GEMV from four rocprofv3 --pmc runs
-    under `d`: pmc_bench_FETCH_SIZE, pmc_bench_WRITE_SIZE (this script's default
-    workload) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE (--mode copy, a
-    256 MiB device copy).  Each counter (KiB per dispatch) is scaled by
-    (known copy bytes) / (what the counter reads for the copy)."""
+def _csv_rows(d, pattern):
     import csv
     import glob
-    import statistics
+    files = glob.glob(os.path.join(d, "**", pattern), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no {pattern} under {d}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
 
+
+def ingest_pmc(d):
+    """Calibrated HBM traffic of the square GEMV from four rocprofv3 --pmc runs
+    under `d`: pmc_bench_FETCH_SIZE, pmc_bench_WRITE_SIZE (--mode
+    profile-square) and pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE (--mode copy,
+    a 256 MiB device copy).  Each counter (KiB per dispatch) is scaled by
+    (known copy bytes) / (what the counter reads for the copy)."""
     def values(sub, pred):
-        f = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)[0]
-        return [float(r["Counter_Value"]) for r in csv.DictReader(open(f)) if pred(r["Kernel_Name"])]
+        rows = _csv_rows(os.path.join(d, sub), "*counter_collection.csv")
+        return [float(r["Counter_Value"]) for r in rows if pred(r["Kernel_Name"])]
 
     copy_kib = 256 * 1024
     out = {"kernel_source_hash": kernel_source_hash(), "unit": "bytes per launch"}
     total = 0.0
-    for ctr, copy_pred in (("FETCH_SIZE", lambda n: "copyBuffer" in n),
-                           ("WRITE_SIZE", lambda n: "copyBuffer" in n)):
-        # the square GEMV at M = 1 (the run also has the M = 7 calls, on the MFMA kernel)
-        gemm = statistics.median(values(f"pmc_bench_{ctr}", lambda n: "k_gemm_valu" in n))
-        cal = statistics.median(values(f"pmc_copy_{ctr}", copy_pred))
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        gemm = statistics.median(values(f"pmc_bench_{ctr}", lambda n: "k_gemm" in n))
+        cal = statistics.median(values(f"pmc_copy_{ctr}", lambda n: "copyBuffer" in n))
         factor = copy_kib / cal
         out[ctr] = {"gemm_kib_per_dispatch": gemm, "copy_kib_per_dispatch": cal, "factor": round(factor, 4),
                     "calibrated_bytes": round(gemm * factor * 1024)}
@@ -485,28 +558,52 @@ def ingest_pmc(d):
     print(json.dumps(out))
 
 
+def ingest_trace(d):
+    """Per-dispatch durations of the matmul kernels from a rocprofv3
+    --kernel-trace run of --mode profile-square (there every dispatch of the
+    square GEMV's kernel is a graph-replayed call: warm-up and timed replays)."""
+    rows = _csv_rows(d, "*kernel_trace.csv")
+    dur = {}
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "k_gemm" in name:
+            dur.setdefault(name, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for name, v in dur.items():
+        v = np.array(v, dtype=np.float64)
+        out[name] = {"dispatches": int(v.size), "mean_ns": round(float(v.mean()), 1),
+                     "median_ns": round(float(np.median(v)), 1), "p10_ns": round(float(np.percentile(v, 10)), 1),
+                     "p90_ns": round(float(np.percentile(v, 90)), 1),
+                     "gbs_at_mean": round(weight_bytes(5120, 5120) / (v.mean() * 1e-9) / 1e9, 1)}
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--extra", action="store_true", help="also time the gate/up and down configs")
+    ap.add_argument("--extra", action="store_true",
+                    help="also time the down projection at M = 2, 4, 8, 16, 32 and the MLP block")
     ap.add_argument("--tower", action="store_true",
                     help="also time the full-tower decode sweep (64 layers + head, 14.1 GB, M = 1 and 7)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the achievable-read-bandwidth calibration")
-    ap.add_argument("--mode", choices=["bench", "copy", "ingest-pmc"], default="bench",
-                    help="copy: run only the PMC calibration copy kernel; ingest-pmc: turn rocprofv3 "
-                         "FETCH_SIZE/WRITE_SIZE outputs (--pmc-dir) into profiles/traffic_square_m1.json")
-    ap.add_argument("--pmc-dir", default=None)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="only the default workload (no square M=7, gate/up, down)")
+    ap.add_argument("--mode", choices=["bench", "profile-square", "copy", "ingest-pmc", "ingest-trace"],
+                    default="bench",
+                    help="profile-square: only the default workload's graph replays (for rocprofv3); "
+                         "copy: the PMC calibration copy; ingest-pmc / ingest-trace: summarise rocprofv3 "
+                         "outputs under --prof-dir")
+    ap.add_argument("--prof-dir", default=None)
     args = ap.parse_args()
     if args.mode == "ingest-pmc":
-        ingest_pmc(args.pmc_dir)
+        ingest_pmc(args.prof_dir)
         return
-    if args.mode == "copy":
-        import torch
-        copy_calibration(torch.device("cuda:0"))
+    if args.mode == "ingest-trace":
+        ingest_trace(args.prof_dir)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -518,28 +615,36 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    r = bench_square(args, dev, stream)
-    log(f"[bench] square (graph replay): {r['per_call']*1e6:.3f} us/call, {r['gbs']:.1f} GB/s; "
-        f"eager: {r['eager_per_call']*1e6:.3f} us/call, {r['eager_gbs']:.1f} GB/s; "
-        f"M=7: {r['m7_per_call']*1e6:.3f} us/call, {r['m7_gbs']:.1f} GB/s")
-    cal = None if args.no_calibration else calibration(dev, stream, r["copies"])
+    if args.mode == "copy":
+        copy_calibration(dev)
+        return
+    if args.mode == "profile-square":
+        profile_square(args, dev, stream)
+        return
+    sq = square_setup(dev)
+    r = bench_square(args, dev, stream, sq)
+    bpc = weight_bytes(sq["N"], sq["K"])
+    gbs = bpc / r["per_call"] / 1e9
+    win_us = [p / sq["copies"] * 1e6 for p in r["per_window"]]
+    log(f"[bench] square M=1 (graph replay): {r['per_call']*1e6:.3f} us/call, {gbs:.1f} GB/s; "
+        f"windows {[round(u, 3) for u in win_us]}")
+    configs = None if args.no_configs else bench_configs(dev, stream, sq, extra=args.extra)
+    cal = None if args.no_calibration else calibration(dev, stream, sq["copies"])
     if cal is not None:
-        cal["value_frac_of_stream"] = round(r["gbs"] / cal["stream_4gib_gbs"], 4)
-        cal["value_frac_of_call_sized"] = round(r["gbs"] / cal["call_sized_gbs"], 4)
-        log(f"[bench] calibration: streaming read {cal['stream_4gib_gbs']} GB/s (4 GiB), "
-            f"{cal['call_sized_gbs']} GB/s ({cal['call_sized_us_per_call']} us per 14.7 MB call)")
-    extra = bench_extra(dev, stream) if args.extra else None
-    if args.tower:
-        extra = dict(extra or {}, **bench_tower(dev, stream))
+        cal["value_frac_of_stream"] = round(gbs / cal["stream_4gib_gbs"], 4)
+        cal["value_frac_of_call_sized"] = round(gbs / cal["call_sized_gbs"], 4)
+        log(f"[bench] calibration: {cal}")
+    tower = bench_tower(dev, stream) if args.tower else None
+    del sq
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": "effective weight GB/s (NVFP4 codes + E4M3 scales + g per call / time per call), W4A16 GEMV",
-        "value": round(r["gbs"], 2),
+        "value": round(gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(r["ms"] / args.steps, 4),
+        "ms_per_step": round(r["total"] * 1e3 / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -548,22 +653,22 @@ def main():
         "config": {"workload": "square projection GEMV, K=5120 N=5120 M=1, 64 byte-identical "
                                "weight copies (943.7 MB) cycled per call; one step = the 64 calls "
                                "captured in one HIP graph and replayed",
-                   "K": r["K"], "N": r["N"], "M": 1, "copies": r["copies"], "calls_timed": r["calls"],
+                   "K": 5120, "N": 5120, "M": 1, "copies": 64, "calls_timed": r["calls"],
                    "us_per_call": round(r["per_call"] * 1e6, 3),
-                   "eager_us_per_call": round(r["eager_per_call"] * 1e6, 3),
-                   "eager_gbs": round(r["eager_gbs"], 1)},
-        "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "traffic": stored_traffic()},
+                   "us_per_call_windows_median": round(statistics.median(win_us), 3),
+                   "us_per_call_windows_min": round(min(win_us), 3), "windows": len(win_us)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic()},
         "cpu_baseline": cpu,
-        # the metric's second operating point: the same workload for a verify
-        # block of M = 7 activation rows (not the `value`)
-        "square_M7": {"us_per_call": round(r["m7_per_call"] * 1e6, 3), "gbs": round(r["m7_gbs"], 2),
-                      "frac": round(r["m7_gbs"] / HBM_PEAK_GBS, 4), "calls_timed": 10 * r["copies"]},
+        # the metric's operating points on the configurations that define them
+        # (M = 1 decode, M = 7 verify block): µs per call, GB/s and fraction of
+        # the HBM peak, median and minimum of 5 timed windows
+        "configs": configs,
         # achievable read rates on this box: `value` against them is "% of achievable"
         "calibration": cal,
     }
-    if extra is not None:
-        line["extra"] = extra
+    if tower is not None:
+        line["tower"] = tower
     print(json.dumps(line), flush=True)
 
 
