@@ -63,6 +63,7 @@ struct Plan {
   int kmax;    // segment slots per wave
   size_t lds;  // dynamic LDS bytes per workgroup
   size_t ws;   // workspace bytes (fp32 partials) when S > 1
+  int rows_cpl; // > 0: the whole-row VALU kernel for K = 1024 * rows_cpl (S = 1)
 };
 
 // ---- kernel registry ---------------------------------------------------------
@@ -93,13 +94,15 @@ struct KernEntry {
   W4A16_VALU_ALL_MT(16, 16, F, 512)                                                \
   W4A16_VALU_ALL_MT(32, 4, F, 1024) W4A16_VALU_ALL_MT(32, 8, F, 512)               \
   W4A16_VALU_ALL_MT(32, 8, F, 1024) W4A16_VALU_ALL_MT(32, 12, F, 512)              \
-  W4A16_VALU_ALL_MT(32, 16, F, 512) W4A16_VALU_ALL_MT(32, 5, F, 1024)
+  W4A16_VALU_ALL_MT(32, 16, F, 512) W4A16_VALU_ALL_MT(32, 5, F, 1024)            \
+  W4A16_VALU_ALL_MT(32, 2, F, 1024)
 #define W4A16_MFMA_SET(F)                                                          \
   W4A16_MFMA_ALL_P(1, 8, F, 512) W4A16_MFMA_ALL_P(1, 16, F, 512)                   \
   W4A16_MFMA_ALL_P(2, 4, F, 512) W4A16_MFMA_ALL_P(2, 8, F, 512)                    \
   W4A16_MFMA_ALL_P(2, 8, F, 1024) W4A16_MFMA_ALL_P(4, 4, F, 512)                   \
   W4A16_ME(5, 1, 4, F, 512) W4A16_ME(6, 1, 4, F, 512) W4A16_ME(7, 1, 4, F, 512)     \
-  W4A16_ME(8, 1, 4, F, 512) W4A16_MFMA_ALL_P(1, 4, F, 512)
+  W4A16_ME(8, 1, 4, F, 512) W4A16_MFMA_ALL_P(1, 4, F, 512)                         \
+  W4A16_MFMA_ALL_P(1, 2, F, 1024) W4A16_MFMA_ALL_P(1, 4, F, 1024)
 #endif
 // the launch rules' variants (the argmax epilogue exists only in these)
 #define W4A16_VALU_BASE(F)                                                         \
@@ -151,9 +154,65 @@ struct Override {
 Override g_override{};
 #endif
 
+// Whole-row VALU kernels (k_gemm_rows): K = 1024 * kRowsCpl, M <= 2, plain
+// and SwiGLU epilogues.  5120 is the hidden size of the model family served
+// here (square projections, gate/up); other K take the general kernels.
+constexpr int kRowsCpl = 5;
+struct RowsEntry {
+  int MT, epi;
+  const void* fn;
+};
+#define W4A16_RE(MT, F) {MT, F, reinterpret_cast<const void*>(&k_gemm_rows<MT, kRowsCpl, F>)},
+const RowsEntry kRowsKernels[] = {W4A16_RE(1, kEpiPlain) W4A16_RE(2, kEpiPlain)
+                                  W4A16_RE(1, kEpiSwiglu) W4A16_RE(2, kEpiSwiglu)};
+#undef W4A16_RE
+const void* find_rows_kernel(int MT, int epi) {
+  for (const RowsEntry& e : kRowsKernels)
+    if (e.MT == MT && e.epi == epi) return e.fn;
+  return nullptr;
+}
+
+// Plan for the whole-row kernel, or false if it does not apply.  One row
+// block per CU; 8 waves when a block has at most 16 tasks (two rows each;
+// fused: one gate/up pair), else 4 (measured on MI355X: square 5120^2 with
+// 10 tasks per block 4.82 us at 8 waves, 5.04 at 10, 5.59 at 4; gate/up
+// 2 x 17408 x 5120 with 68 tasks per block 17.6 us at 4 waves, 17.9 at 8).
+bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
+  if (M > kValuMaxM || epi == kEpiArgmax || K != 1024 * kRowsCpl) return false;
+#ifdef W4A16_TUNING
+  if (g_override.enable) return false;
+#endif
+  if (!find_rows_kernel(M, epi)) return false;
+  const int RT = epi == kEpiSwiglu ? 1 : 2;
+  const long long tasks = ((long long)N + RT - 1) / RT;
+  long long nrb = cu_count();
+  if (nrb > tasks) nrb = tasks;
+  if (nrb < 1) nrb = 1;
+  const int rq = N / (int)nrb, rr = N % (int)nrb;
+  const long long per_block = ((long long)rq + (rr > 0) + RT - 1) / RT;
+  pl = Plan{};
+  pl.mfma = false;
+  pl.lr = 32;
+  pl.W = per_block <= 16 ? 8 : 4;   // the kernel stages x with >= 4 waves
+  pl.LB = M == 1 ? 640 : 512;
+  pl.nrb = (int)nrb;
+  pl.S = 1;
+  pl.rq = rq;
+  pl.rr = rr;
+  pl.lds = (size_t)M * (size_t)(4 * (K >> 5) + 1) * 16;
+  pl.ws = 0;
+  pl.rows_cpl = kRowsCpl;
+  return true;
+}
+
 // Kernel selection is a pure function of (M, N, K, epilogue) and the device's
-// compute-unit count.
-Plan plan_gemm(int M, int N, int K, int epi) {
+// compute-unit count.  rows_ok: whether the whole-row kernel may be chosen
+// (the persistent MLP kernel runs the general kernels' bodies only).
+Plan plan_gemm(int M, int N, int K, int epi, bool rows_ok = true) {
+  {
+    Plan r;
+    if (rows_ok && plan_rows(M, N, K, epi, r)) return r;
+  }
   const bool fused = epi == kEpiSwiglu;
   Plan pl{};
   const int cus = cu_count();
@@ -302,6 +361,12 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t
 }
 
 hipError_t dispatch(const Plan& pl, int epi, hipStream_t s, const MatArgs& a) {
+  if (pl.rows_cpl > 0) {
+    const void* fn = find_rows_kernel(a.M, epi);
+    if (!fn || pl.W < 4 || pl.W * 64 > pl.LB || a.K != 1024 * pl.rows_cpl)
+      return hipErrorInvalidConfiguration;
+    return launch(fn, dim3((unsigned)pl.nrb), dim3((unsigned)(pl.W * 64)), pl.lds, s, a);
+  }
   const int rows = pl.mfma ? (a.M + 3) / 4 : a.M;
   const KernEntry* k = find_kernel(pl.mfma, rows, pl.lr, pl.D, epi, pl.LB);
   if (!k || pl.W * 64 > pl.LB) return hipErrorInvalidConfiguration;
@@ -391,8 +456,10 @@ struct MlpPlan {
 
 MlpPlan plan_mlp(int M, int H, int F) {
   MlpPlan mp{};
-  mp.p1 = plan_gemm(M, F, H, kEpiSwiglu);
-  mp.p2 = plan_gemm(M, H, F, kEpiPlain);
+  // the general kernels' plans: the persistent kernel runs their bodies, and
+  // their workspace covers every variant (the whole-row kernel needs none)
+  mp.p1 = plan_gemm(M, F, H, kEpiSwiglu, false);
+  mp.p2 = plan_gemm(M, H, F, kEpiPlain, false);
   if (mp.p1.S == 0 || mp.p2.S == 0) return MlpPlan{};
   const size_t h_bytes = align256((size_t)M * F * 2);
   const size_t w1 = mp.p1.ws > 0 ? align256(mp.p1.ws - kCounterBytes) : 0;
@@ -485,8 +552,16 @@ w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace
     if (e == hipSuccess) return W4A16_OK;
     (void)hipGetLastError();  // clear the refused launch's error
   }
-  hipError_t e = dispatch(mp.p1, kEpiSwiglu, stream, up);
-  if (e == hipSuccess) e = dispatch(mp.p2, kEpiPlain, stream, down);
+  // two launches: each phase takes its own best plan
+  const Plan q1 = plan_gemm(M, F, H, kEpiSwiglu), q2 = plan_gemm(M, H, F, kEpiPlain);
+  if (q1.S == 0 || q2.S == 0 || q1.lds > kMaxLds || q2.lds > kMaxLds || q1.ws > mp.p1.ws ||
+      q2.ws > mp.p2.ws)
+    return W4A16_ERR_UNSUPPORTED;
+  prepare(up, q1, reinterpret_cast<int*>(w), reinterpret_cast<float*>(w + mp.part1));
+  prepare(down, q2, reinterpret_cast<int*>(w + kCounterBytes),
+          reinterpret_cast<float*>(w + mp.part2));
+  hipError_t e = dispatch(q1, kEpiSwiglu, stream, up);
+  if (e == hipSuccess) e = dispatch(q2, kEpiPlain, stream, down);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }
 

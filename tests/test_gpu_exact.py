@@ -99,13 +99,13 @@ def test_tiny_config_exact():
     gemm_exact(1, c["N"], c["K"], 900, ctx="tiny")
 
 
-@pytest.mark.parametrize("M", [1, 7])
+@pytest.mark.parametrize("M", [1, 2, 7])
 @pytest.mark.parametrize("scales", ["pow2", "mant"])
 def test_square_config_exact(M, scales):
     gemm_exact(M, 5120, 5120, 910 + M, scales, ctx="square")
 
 
-@pytest.mark.parametrize("M", [1, 7])
+@pytest.mark.parametrize("M", [1, 2, 7])
 def test_gate_up_config_exact(M):
     fused_exact(M, 17408, 5120, 920 + M, ctx="gate_up")
 
@@ -138,6 +138,24 @@ def test_fused_every_family_ragged_n_exact(M):
                                    (7, 4096, 1024), (1, 300, 33024)])
 def test_small_and_extreme_shapes_exact(M, N, K):
     gemm_exact(M, N, K, 1200 + M + N, ctx="shape")
+
+
+# ---- the whole-row kernel (K = 5120, M <= 2): row-block and task edges ---------
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("N", [1, 2, 3, 255, 256, 257, 511, 513, 2561, 4097, 5121])
+def test_whole_row_kernel_ragged_n_exact(M, N):
+    """N below, at and just past multiples of the CU count and of two rows per
+    task: blocks with no task, a task with one live row, uneven blocks."""
+    gemm_exact(M, N, 5120, 1600 + 7 * M + N, "mant" if N % 2 else "pow2", ctx="rows")
+
+
+@pytest.mark.parametrize("M", [1, 2])
+@pytest.mark.parametrize("N", [1, 3, 257, 4099, 8193])
+def test_whole_row_kernel_fused_ragged_n_exact(M, N):
+    """Fused tasks are one gate/up pair: 8 waves per block up to 16 pairs
+    (N <= 4096 on 256 CUs), 4 above."""
+    fused_exact(M, N, 5120, 1700 + 7 * M + N, ctx="rows fused")
 
 
 # ---- one-hot sweep: every 32-input chunk position of K = 5120 -----------------
