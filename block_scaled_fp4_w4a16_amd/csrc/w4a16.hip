@@ -154,23 +154,28 @@ struct Override {
 Override g_override{};
 #endif
 
-// Whole-row VALU kernels (k_gemm_rows): K = 1024 * kRowsCpl, M <= 2, plain
-// and SwiGLU epilogues.  5120 is the hidden size of the model family served
-// here (square projections, gate/up); other K take the general kernels.
-constexpr int kRowsCpl = 5;
+// Whole-row VALU kernels (k_gemm_rows), by K = 1024 * CPL: 5120, the hidden
+// size of the model family served here (square projections, gate/up), for
+// M <= 2 and both epilogues.  Other shapes take the general kernels.  (The
+// same kernel at K = 17408, the down projection, M = 1: 14.0-15.1 us at
+// 4-8 waves against 10.8 us for the general VALU kernel -- ten tasks of 17
+// steps per CU leave the waves unevenly loaded and the per-wave step chain
+// long; measured on MI355X.)
 struct RowsEntry {
-  int MT, epi;
+  int MT, cpl, epi;
   const void* fn;
 };
-#define W4A16_RE(MT, F) {MT, F, reinterpret_cast<const void*>(&k_gemm_rows<MT, kRowsCpl, F>)},
-const RowsEntry kRowsKernels[] = {W4A16_RE(1, kEpiPlain) W4A16_RE(2, kEpiPlain)
-                                  W4A16_RE(1, kEpiSwiglu) W4A16_RE(2, kEpiSwiglu)};
+#define W4A16_RE(MT, CPL, F) {MT, CPL, F, reinterpret_cast<const void*>(&k_gemm_rows<MT, CPL, F>)},
+const RowsEntry kRowsKernels[] = {W4A16_RE(1, 5, kEpiPlain) W4A16_RE(2, 5, kEpiPlain)
+                                  W4A16_RE(1, 5, kEpiSwiglu) W4A16_RE(2, 5, kEpiSwiglu)};
 #undef W4A16_RE
-const void* find_rows_kernel(int MT, int epi) {
+const void* find_rows_kernel(int MT, int cpl, int epi) {
   for (const RowsEntry& e : kRowsKernels)
-    if (e.MT == MT && e.epi == epi) return e.fn;
+    if (e.MT == MT && e.cpl == cpl && e.epi == epi) return e.fn;
   return nullptr;
 }
+// launch bound of k_gemm_rows<MT, CPL, ...> (as in its declaration)
+int rows_launch_bound(int MT, int cpl) { return (MT == 1 && cpl <= 8) ? 640 : 512; }
 
 // Plan for the whole-row kernel, or false if it does not apply.  One row
 // block per CU; 8 waves when a block has at most 16 tasks (two rows each;
@@ -178,11 +183,12 @@ const void* find_rows_kernel(int MT, int epi) {
 // 10 tasks per block 4.82 us at 8 waves, 5.04 at 10, 5.59 at 4; gate/up
 // 2 x 17408 x 5120 with 68 tasks per block 17.6 us at 4 waves, 17.9 at 8).
 bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
-  if (M > kValuMaxM || epi == kEpiArgmax || K != 1024 * kRowsCpl) return false;
+  if (M > kValuMaxM || epi == kEpiArgmax || K % 1024 != 0) return false;
 #ifdef W4A16_TUNING
   if (g_override.enable) return false;
 #endif
-  if (!find_rows_kernel(M, epi)) return false;
+  const int cpl = K / 1024;
+  if (!find_rows_kernel(M, cpl, epi)) return false;
   const int RT = epi == kEpiSwiglu ? 1 : 2;
   const long long tasks = ((long long)N + RT - 1) / RT;
   long long nrb = cu_count();
@@ -194,14 +200,14 @@ bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
   pl.mfma = false;
   pl.lr = 32;
   pl.W = per_block <= 16 ? 8 : 4;   // the kernel stages x with >= 4 waves
-  pl.LB = M == 1 ? 640 : 512;
+  pl.LB = rows_launch_bound(M, cpl);
   pl.nrb = (int)nrb;
   pl.S = 1;
   pl.rq = rq;
   pl.rr = rr;
   pl.lds = (size_t)M * (size_t)(4 * (K >> 5) + 1) * 16;
   pl.ws = 0;
-  pl.rows_cpl = kRowsCpl;
+  pl.rows_cpl = cpl;
   return true;
 }
 
@@ -362,7 +368,7 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t
 
 hipError_t dispatch(const Plan& pl, int epi, hipStream_t s, const MatArgs& a) {
   if (pl.rows_cpl > 0) {
-    const void* fn = find_rows_kernel(a.M, epi);
+    const void* fn = find_rows_kernel(a.M, pl.rows_cpl, epi);
     if (!fn || pl.W < 4 || pl.W * 64 > pl.LB || a.K != 1024 * pl.rows_cpl)
       return hipErrorInvalidConfiguration;
     return launch(fn, dim3((unsigned)pl.nrb), dim3((unsigned)(pl.W * 64)), pl.lds, s, a);

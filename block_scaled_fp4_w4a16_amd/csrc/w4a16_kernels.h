@@ -787,7 +787,9 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 
 // ---------------------------------------------------------------------------
 // Whole-row VALU kernel: M = MT in {1, 2}, K = 1024 * CPL fixed at compile
-// time, no K split; plain and gate/up + SwiGLU epilogues.
+// time, no K split; plain and gate/up + SwiGLU epilogues.  Launch bound 640
+// threads for short rows at M = 1, else 512 (two tasks of CPL loads per lane
+// in registers).
 //
 // A task is two weight rows (fused: a gate row and the same up row): lanes
 // 0-31 take the first, lanes 32-63 the second, and at step jj lane p reads
@@ -812,7 +814,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 // general VALU kernel; gate/up 2 x 17408 x 5120 17.6 against 18.0 us.
 // ---------------------------------------------------------------------------
 template <int MT, int CPL, int EPI>
-__global__ void __launch_bounds__(MT == 1 ? 640 : 512) k_gemm_rows(MatArgs a) {
+__global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows(MatArgs a) {
   static_assert(EPI != kEpiArgmax, "plain and SwiGLU epilogues only");
   constexpr bool FUSED = EPI == kEpiSwiglu;
   constexpr int L = 32;                    // lanes per weight row
