@@ -37,6 +37,11 @@ class W4A16Error(RuntimeError):
         super().__init__(f"{what}: {status_string(status)} (status {status})")
 
 
+class MlpBarrierTimeout(RuntimeError):
+    """A one-launch MLP call stopped waiting at its grid barrier: its y is
+    undefined (the workspace's time-out flag is set)."""
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -271,12 +276,16 @@ def new_workspace_mlp(M: int, H: int, F: int, device):
 
 
 def mlp_swiglu(gate, up, down, x, y=None, workspace=None, stream=None, one_launch=False,
-               spin_limit=-1):
+               spin_limit=-1, check_barrier=True):
     """y[M, H] = bf16(bf16(silu(x @ Wg^T) * (x @ Wu^T)) @ Wd^T): one MLP block.
     gate, up, down: (wq, ws, g) tuples; Wg, Wu are [F][H], Wd is [H][F].
     one_launch: run both matmuls in one cooperative persistent launch when
     the shape and the stream allow it (bit-identical to two launches);
-    spin_limit: the barrier's poll limit (< 0: the library default)."""
+    spin_limit: the barrier's poll limit (< 0: the library default).
+    check_barrier: after a one-launch call on a stream that is not being
+    captured, wait for it and raise MlpBarrierTimeout if its barrier timed
+    out (leaving the flag set); False skips that synchronisation, and the
+    caller reads the flag with mlp_timed_out()."""
     F, H = _weights(*gate, "gate ")
     if _weights(*up, "up ") != (F, H):
         raise ValueError("gate and up weights must have the same shape")
@@ -301,6 +310,13 @@ def mlp_swiglu(gate, up, down, x, y=None, workspace=None, stream=None, one_launc
                                 _ptr(workspace), wbytes, ctypes.byref(opts), _stream(stream))
     if st != OK:
         raise W4A16Error(st, "w4a16_mlp_swiglu")
+    if one_launch and check_barrier and workspace is not None and \
+            not torch.cuda.is_current_stream_capturing():
+        s = stream if stream is not None else torch.cuda.current_stream(x.device)
+        s.synchronize()
+        flag = workspace[MLP_TIMEOUT_OFFSET:MLP_TIMEOUT_OFFSET + 4].view(torch.int32).item()
+        if flag != 0:
+            raise MlpBarrierTimeout("w4a16_mlp_swiglu: the one-launch barrier timed out; y is undefined")
     return y
 
 

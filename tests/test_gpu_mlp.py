@@ -143,8 +143,14 @@ def test_barrier_timeout_is_flagged_and_recovers():
     dx = d_bf16(x)
     work = w4.new_workspace_mlp(M, H, F, "cuda")
     say("[mlp timeout] poll limit 0")
-    # every workgroup but the last to arrive gives up at once
-    w4.mlp_swiglu(*dev, dx, workspace=work, one_launch=True, spin_limit=0)
+    # every workgroup but the last to arrive gives up at once; the binding
+    # reports it (eager call) ...
+    with pytest.raises(w4.MlpBarrierTimeout):
+        w4.mlp_swiglu(*dev, dx, workspace=work, one_launch=True, spin_limit=0)
+    assert w4.mlp_timed_out(work)
+    work[w4.MLP_TIMEOUT_OFFSET:w4.MLP_TIMEOUT_OFFSET + 4] = 0
+    # ... or leaves it to the caller
+    w4.mlp_swiglu(*dev, dx, workspace=work, one_launch=True, spin_limit=0, check_barrier=False)
     assert w4.mlp_timed_out(work)
     work[w4.MLP_TIMEOUT_OFFSET:w4.MLP_TIMEOUT_OFFSET + 4] = 0
     assert counters_zero(work), "counters must be reset even after a time-out"
