@@ -146,6 +146,7 @@ W4A16_DEV float load_f32_vmem(const float* g) {
 // there, so that no XCD reads a stale copy.
 constexpr int kCoPlain = 0, kCoLoadX = 1, kCoStoreY = 2;
 constexpr int kCpolSc1 = 16;  // cache-policy bits of a memory instruction: device scope
+constexpr int kCpolNt = 2;    // ... and non-temporal (the weight streams)
 
 // 16 bytes at base[i]; with XC, read at device scope (buffer load, sc1).
 // The byte offset i * 16 must stay below 2^31.
@@ -816,6 +817,7 @@ __global__ void __launch_bounds__(LB) k_gemm_valu(MatArgs a) {
 template <int MT, int CPL, int EPI>
 __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows(MatArgs a) {
   static_assert(EPI != kEpiArgmax, "plain and SwiGLU epilogues only");
+  W4A16_STAMP(t_start);
   constexpr bool FUSED = EPI == kEpiSwiglu;
   constexpr int L = 32;                    // lanes per weight row
   constexpr int RT = FUSED ? 1 : 2;        // output rows per task
@@ -859,17 +861,38 @@ __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows
   uint4 qa[CPL], qb[CPL];
   uint32_t sa[CPL], sb[CPL];
   auto load_task = [&](uint4 (&q)[CPL], uint32_t (&sc)[CPL], int t) {
-    int row = row_lo + t * RT + (FUSED ? 0 : r);
-    row = row < row_hi ? row : row_hi - 1;
-    const bool live = t < ntasks;
-    const uint8_t* qr = live ? wq + (size_t)row * (K >> 1) : xbase;
-    const uint8_t* sr = live ? ws + (size_t)row * (K >> 4) : xbase;
-    const uint4* qp = reinterpret_cast<const uint4*>(qr) + p;
-    const uint32_t* sp = reinterpret_cast<const uint32_t*>(sr) + (p >> 1);
+    if constexpr (!FUSED) {
+      // both rows of the task through one buffer resource each for codes and
+      // scales; a task past the wave's last one gets 0 records, so its loads
+      // return zeros without touching memory
+      const int row0 = row_lo + t * RT;
+      const int live = t < ntasks ? (row_hi - row0 < 2 ? row_hi - row0 : 2) : 0;
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(wq) + (size_t)(live ? row0 : 0) * (K >> 1), (short)0,
+          live * (K >> 1), kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(ws) + (size_t)(live ? row0 : 0) * (K >> 4), (short)0,
+          live * (K >> 4), kBufferWord3);
+      const int qo = r * (K >> 1) + p * 16, so = r * (K >> 4) + (p >> 1) * 4;
 #pragma unroll
-    for (int jj = 0; jj < CPL; ++jj) {
-      q[jj] = load_stream(qp + L * jj);
-      sc[jj] = __builtin_nontemporal_load(sp + (L / 2) * jj);
+      for (int jj = 0; jj < CPL; ++jj) {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rq, qo + 16 * L * jj, 0, kCpolNt);
+        q[jj] = make_uint4(v.x, v.y, v.z, v.w);
+        sc[jj] = __builtin_amdgcn_raw_buffer_load_b32(rs, so + 2 * L * jj, 0, kCpolNt);
+      }
+    } else {
+      int row = row_lo + t * RT;
+      row = row < row_hi ? row : row_hi - 1;
+      const bool live = t < ntasks;
+      const uint8_t* qr = live ? wq + (size_t)row * (K >> 1) : xbase;
+      const uint8_t* sr = live ? ws + (size_t)row * (K >> 4) : xbase;
+      const uint4* qp = reinterpret_cast<const uint4*>(qr) + p;
+      const uint32_t* sp = reinterpret_cast<const uint32_t*>(sr) + (p >> 1);
+#pragma unroll
+      for (int jj = 0; jj < CPL; ++jj) {
+        q[jj] = load_stream(qp + L * jj);
+        sc[jj] = __builtin_nontemporal_load(sp + (L / 2) * jj);
+      }
     }
   };
   auto compute = [&](const uint4 (&q)[CPL], const uint32_t (&sc)[CPL], int t) {
@@ -944,8 +967,13 @@ __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows
     ig0 = 1.0f / *reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(a.g0));
     if (FUSED) ig1 = 1.0f / *reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(a.g1));
   }
+  W4A16_STAMP(t_issued);
   // workgroup barrier for the LDS stores only (the weight loads stay in flight)
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  W4A16_STAMP(t_barrier);
+#ifdef W4A16_TRACE
+  unsigned long long t_first = 0;
+#endif
   // Two tasks per iteration and one exit test.  An exit between the two
   // halves would merge the state "next task's loads pending" into the loop
   // head, where the compiler then waits for every load before issuing the
@@ -957,11 +985,18 @@ __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows
     load_task(qb, sb, t + W);
     __builtin_amdgcn_sched_barrier(0);
     compute(qa, sa, t);
+#ifdef W4A16_TRACE
+    if (t_first == 0) t_first = wall_clock64();
+#endif
     load_task(qa, sa, t + 2 * W);
     __builtin_amdgcn_sched_barrier(0);
     if (t + W < ntasks) compute(qb, sb, t + W);
     t += 2 * W;
   }
+#ifdef W4A16_TRACE
+  W4A16_STAMP(t_end);
+  W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_end);
+#endif
 }
 
 // ---------------------------------------------------------------------------
