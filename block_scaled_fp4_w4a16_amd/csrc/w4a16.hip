@@ -41,6 +41,7 @@ constexpr size_t kMaxLds = 160 * 1024 - 256;
 // another call's counters.  The fp32 partials follow it.
 constexpr size_t kCounterBytes = 4096;
 constexpr int kMaxSplitRowBlocks = (int)(kCounterBytes / sizeof(int));
+static_assert(kArgmaxSplitCounter == kMaxSplitRowBlocks - 1, "argmax counter: the last of the area");
 
 // Activation rows up to which the VALU kernel runs; the MFMA kernel takes
 // the rest.  Its cost is flat up to four rows while the VALU kernel's grows
@@ -298,7 +299,10 @@ Plan plan_gemm(int M, int N, int K, int epi, bool rows_ok = true) {
 #endif
     if (nrb > groups) nrb = groups;
     if (nrb > N) nrb = N;
-    if (S > 1 && nrb > kMaxSplitRowBlocks) nrb = kMaxSplitRowBlocks;
+    // split-K arrival counters, one per row block (a K-split argmax keeps the
+    // last counter for its final reduction)
+    const int max_rb = kMaxSplitRowBlocks - (epi == kEpiArgmax ? 1 : 0);
+    if (S > 1 && nrb > max_rb) nrb = max_rb;
     const int rq = N / (int)nrb, rr = N % (int)nrb;
     const long long ntasks = ((long long)rq + (rr > 0) + RT - 1) / RT;  // tasks of the largest block
     const int CPL = pl.mfma ? (CRS + 15) / 16 : CRS / pl.lr;
@@ -331,8 +335,8 @@ Plan plan_gemm(int M, int N, int K, int epi, bool rows_ok = true) {
     // quotients in the kernels (div_small) are exact below 2^23
     if (TS * (W + 1) >= (1LL << 23) || (long long)xrows * CRS * 4 + 1024LL * 16 >= (1LL << 23))
       return Plan{};
-    // argmax takes whole rows: no K split
-    if (epi == kEpiArgmax && S > 1) break;
+    // argmax with a K split: the MFMA kernel only (M >= 3)
+    if (epi == kEpiArgmax && S > 1 && !pl.mfma) break;
     pl.S = S;
     pl.nrb = (int)nrb;
     pl.rq = rq;
@@ -341,9 +345,10 @@ Plan plan_gemm(int M, int N, int K, int epi, bool rows_ok = true) {
     pl.kmax = (int)kmax;
     pl.lds = lds;
     if (epi == kEpiArgmax) {
-      // argmax: the arrival counter, then one (value, index) candidate per
-      // workgroup and activation row
-      pl.ws = kCounterBytes + (size_t)pl.nrb * (size_t)M * 2 * sizeof(float);
+      // argmax: the arrival counters, the fp32 partials of a K split, then
+      // one (value, index) candidate per row block and activation row
+      pl.ws = kCounterBytes + (S > 1 ? (size_t)S * (size_t)M * (size_t)N * sizeof(float) : 0) +
+              (size_t)pl.nrb * (size_t)M * 2 * sizeof(float);
     } else {
       pl.ws = S > 1 ? kCounterBytes +
                           (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1)
@@ -418,6 +423,8 @@ w4a16_status_t run_matmul(MatArgs a, int epi, void* workspace, size_t workspace_
   if (pl.ws > 0 && !aligned(workspace, 16)) return W4A16_ERR_UNSUPPORTED;
   prepare(a, pl, static_cast<int*>(workspace),
           reinterpret_cast<float*>(static_cast<char*>(workspace) + kCounterBytes));
+  // argmax candidates follow the partials of a K split
+  if (epi == kEpiArgmax && pl.S > 1) a.cand = a.part + (size_t)pl.S * (size_t)a.M * (size_t)a.N;
   const hipError_t e = dispatch(pl, epi, stream, a);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
 }

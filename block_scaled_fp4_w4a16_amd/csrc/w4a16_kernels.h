@@ -364,9 +364,27 @@ W4A16_DEV float splitk_sum(const float* p, size_t st, int S) {
   return v;
 }
 
-template <bool FUSED, bool YC>
+// Index of an argmax candidate that has seen no row yet.
+constexpr int kNoIndex = 0x7fffffff;
+
+// Counter of the argmax epilogue's final reduction when the call is split
+// along K (the row blocks' split-K counters take cnt[0 .. nrb-1], nrb < this).
+constexpr int kArgmaxSplitCounter = 1023;
+
+template <int MB>
+W4A16_DEV void argmax_finish(const MatArgs& a, int* cnt, int nwg, float* red, int W);
+template <int MB>
+W4A16_DEV void wg_argmax_rows(float (&v)[MB], int (&ix)[MB], int M, float* red, int W);
+W4A16_DEV void argmax_take(float& bv, int& bi, float v, int i);
+
+// EPI == kEpiArgmax: the finishing workgroup of each row block turns its
+// rows' summed logits into one (value, index) candidate per activation row
+// (MB >= M rows, side by side), stores them, and the last row block to do so
+// reduces every row block's candidates (argmax_finish).  red: LDS scratch of
+// 2 * MB floats per wave; W: waves per workgroup; nrb: row blocks.
+template <bool FUSED, bool YC, int EPI = kEpiPlain, int MB = 1>
 W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, float ig0,
-                             float ig1) {
+                             float ig1, float* red = nullptr, int W = 0, int nrb = 0) {
   __shared__ int is_last;
   __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
   __syncthreads();                // ... and so have every other wave's
@@ -376,6 +394,36 @@ W4A16_DEV void splitk_finish(const MatArgs& a, int rb, int row_lo, int nrows, fl
     if (is_last) __hip_atomic_store(a.cnt + rb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  if (EPI == kEpiArgmax) {
+    // only each row block's finishing workgroup arrives at the final
+    // reduction's counter (nrb arrivals in all)
+    if (!is_last) return;
+    const size_t MN = (size_t)a.M * a.N;
+    const int M = a.M;
+    float bv[MB];
+    int bi[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      bv[m] = -__builtin_inff();
+      bi[m] = kNoIndex;
+    }
+    for (int n = threadIdx.x; n < nrows; n += blockDim.x) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        if (m < M) {
+          const size_t i = (size_t)m * a.N + row_lo + n;
+          argmax_take(bv[m], bi[m], splitk_sum(a.part + i, MN, a.S) * ig0, row_lo + n);
+        }
+    }
+    wg_argmax_rows<MB>(bv, bi, M, red, W);
+    if ((int)threadIdx.x < M) {
+      float* c = a.cand + ((size_t)rb * M + threadIdx.x) * 2;
+      store_coherent(c, bv[0]);
+      store_coherent(c + 1, __int_as_float(bi[0]));
+    }
+    argmax_finish<MB>(a, a.cnt + kArgmaxSplitCounter, nrb, red, W);
+    return;
+  }
   if (!is_last) return;
   const size_t MN = (size_t)a.M * a.N;
   for (int o = threadIdx.x; o < nrows * a.M; o += blockDim.x) {
@@ -406,7 +454,6 @@ W4A16_DEV void argmax_take(float& bv, int& bi, float v, int i) {
     bi = i;
   }
 }
-constexpr int kNoIndex = 0x7fffffff;
 
 // Workgroup-wide argmax of up to MB activation rows at once: every thread
 // brings one candidate (v[m], ix[m]) per row m; afterwards thread m (m < M)
@@ -449,14 +496,14 @@ W4A16_DEV void wg_argmax_rows(float (&v)[MB], int (&ix)[MB], int M, float* red, 
 // thread issues the loads of all its candidates' rows before using any of
 // them (they come from beyond the XCD caches: one round trip, not one per row).
 template <int MB>
-W4A16_DEV void argmax_finish(const MatArgs& a, int nwg, float* red, int W) {
+W4A16_DEV void argmax_finish(const MatArgs& a, int* cnt, int nwg, float* red, int W) {
   __shared__ int is_last;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int before = __hip_atomic_fetch_add(a.cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int before = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     is_last = before == nwg - 1;
-    if (is_last) __hip_atomic_store(a.cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (is_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!is_last) return;
@@ -754,7 +801,7 @@ W4A16_DEV void gemm_valu(const MatArgs& a, int rb, int ks, int nwg) {
       store_coherent(c, bv[0]);
       store_coherent(c + 1, __int_as_float(bi[0]));
     }
-    argmax_finish<MT>(a, nwg, red, W);
+    argmax_finish<MT>(a, a.cnt, nwg, red, W);
   } else
   for (int n = tid; n < nrows; n += NT) {
     const int t = n / RT, rt = n - t * RT;
@@ -1265,9 +1312,8 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
   lds_barrier();
   const int M = a.M;
   const int nrows = row_hi - row_lo;
-  if (EPI == kEpiArgmax) {
-    // S == 1 here (the host rejects a K split with this epilogue); x is no
-    // longer needed, so its LDS holds the reduction scratch
+  if (EPI == kEpiArgmax && S == 1) {
+    // x is no longer needed, so its LDS holds the reduction scratch
     float* red = reinterpret_cast<float*>(xs);
     constexpr int MB = 4 * P;
     float bv[MB];
@@ -1302,9 +1348,10 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
       store_coherent(c, bv[0]);
       store_coherent(c + 1, __int_as_float(bi[0]));
     }
-    argmax_finish<MB>(a, nwg, red, W);
+    argmax_finish<MB>(a, a.cnt, nwg, red, W);
   } else
-  // item o = n * 4P + m (rows m >= M are skipped): a constant divisor
+  // item o = n * 4P + m (rows m >= M are skipped): a constant divisor.  With
+  // a K split every epilogue (argmax too) parks fp32 partials first.
   for (int o = tid; o < nrows * 4 * P; o += NT) {
     const int n = o / (4 * P), m = o - n * (4 * P);
     if (m >= M) continue;
@@ -1330,7 +1377,9 @@ W4A16_DEV void gemm_mfma(const MatArgs& a, int rb, int ks, int nwg) {
       store_y<YC>(a.y, (size_t)m * a.N + row, f32_to_bf16(v * ig0));
     }
   }
-  if (S > 1) splitk_finish<FUSED, YC>(a, rb, row_lo, row_hi - row_lo, ig0, ig1);
+  if (S > 1)
+    splitk_finish<FUSED, YC, EPI, 4 * P>(a, rb, row_lo, row_hi - row_lo, ig0, ig1,
+                                        reinterpret_cast<float*>(xs), W, nwg);
 #ifdef W4A16_TRACE
   W4A16_STAMP(t_done);
   W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);

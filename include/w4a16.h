@@ -135,9 +135,12 @@ w4a16_status_t w4a16_gemm_gate_up_swiglu(const uint8_t* wq_gate, const uint8_t* 
  * greedy sampling among its kernels and an option fusing the lm_head with a
  * greedy argmax that avoids the logits buffer (its "CUDA Runtime Knobs").
  *   idx : int32 [M], val : fp32 [M], both device memory, 4-byte aligned.
- *   Other pointers, alignment and shape rules as w4a16_gemm, except that the
- *   shape must not need a K split (the x rows a workgroup stages, M * K bf16
- *   rounded up to whole passes, must fit in LDS), else W4A16_ERR_UNSUPPORTED.
+ *   Other pointers, alignment and shape rules as w4a16_gemm (1 <= M <= 32).
+ *   At 1 <= M <= 2 the shape must not need a K split (the x rows a
+ *   workgroup stages must fit in LDS; K = 5120 fits), else
+ *   W4A16_ERR_UNSUPPORTED; from M = 3 on a K split is taken when x needs it
+ *   (at K = 5120, M > 12): fp32 partial logits go through the workspace and
+ *   the last workgroup of each row block forms its candidates.
  *   workspace : at least w4a16_workspace_size_argmax(M, N, K) bytes (never 0
  *               for a supported shape), 16-byte aligned; its first 4096 bytes
  *               must be zero before the first call and are left zero by

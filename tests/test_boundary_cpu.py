@@ -180,10 +180,12 @@ def test_argmax_argument_checks(lib):
     assert call(work=0, wbytes=0) == w4.ERR_INVALID_VALUE     # the workspace is always required
     assert call(idx=P + 2) == w4.ERR_UNSUPPORTED
     assert call(M=33) == w4.ERR_UNSUPPORTED
-    assert w4.workspace_size_argmax(13, 1000, 5120) == 0       # 13 x rows of 5120 need a K split
-    assert w4.workspace_size_argmax(12, 1000, 5120) > 0
+    # 13 x rows of 5120 need a K split: the workspace then also holds fp32 partial logits
+    assert w4.workspace_size_argmax(13, 1000, 5120) >= 4096 + 2 * 13 * 1000 * 4
+    assert 4096 < w4.workspace_size_argmax(12, 1000, 5120) < 4096 + 12 * 1000 * 4
     assert w4.workspace_size_argmax(1, 248320, 5120) >= 4096 + 8
-    assert w4.workspace_size_argmax(16, 64, 17408) == 0        # would need a K split
+    assert w4.workspace_size_argmax(16, 64, 17408) >= 4096 + 16 * 64 * 4
+    assert w4.workspace_size_argmax(2, 64, 65536) == 0         # M <= 2 takes no K split
 
 
 # ---- MLP block -----------------------------------------------------------------

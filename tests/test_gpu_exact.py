@@ -218,6 +218,30 @@ def test_head_argmax_exact_winner(M):
     assert int(work[:4096].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("M,N", [(13, 4099), (16, 4099), (24, 1031), (32, 4099), (16, 65536)])
+def test_argmax_with_k_split_exact_winner(M, N):
+    """From M = 13 at K = 5120 the x rows exceed the LDS next to the scratch,
+    so the argmax call splits K: partial logits go through the workspace, the
+    last workgroup of each row block forms its candidates, the last row block
+    reduces them.  Exact logits make the winner and its value unique."""
+    K = 5120
+    wq, ws, g, x = exact.exact_gemm_case(1450 + M + N, M, N, K)
+    say(f"[exact argmax split-K] M={M} N={N} K={K}")
+    need = w4.workspace_size_argmax(M, N, K)
+    assert need > 4096 + 4 * M * N, "a K split keeps fp32 partial logits in the workspace"
+    work = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ref, a = oracle.gemm(wq, ws, g, x, M, N, K, nthreads=NTHREADS)
+    exact.assert_exact_regime(a, g, "pow2", "argmax split-K")
+    want_idx = np.argmax(ref, axis=1)
+    want_val = ref[np.arange(M), want_idx]
+    for call in range(2):   # the counters are left zero, so the workspace is reusable
+        idx, val = w4.gemm_argmax(d_u8(wq), d_u8(ws), d_g(g), d_bf16(x), workspace=work)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), want_idx), (call, idx.cpu().numpy(), want_idx)
+        assert np.array_equal(val.cpu().numpy().astype(np.float64), want_val), call
+        assert int(work[:4096].count_nonzero()) == 0
+
+
 # ---- the MLP block, full size ------------------------------------------------
 
 @pytest.mark.parametrize("M", [1, 7])
