@@ -509,6 +509,55 @@ def cpu_baseline(window_s=3.0):
                 cpu_model=cpu_model(), nproc=os.cpu_count(), affinity_cpus=affinity)
 
 
+def cpu_baseline_tower(Ms=(1, 7), layers=64):
+    """The CPU oracle's time per decode token of the full tower, extrapolated
+    from one timed oracle call per matrix shape (all host threads): per token
+    `layers` x (gate/up + SwiGLU, down, 4 square projections) + the head.  A
+    token of the tower takes the oracle tens of seconds (minutes at M = 7),
+    so it is not run whole.  The inputs are seeded random codes and scales of
+    the real shapes (the oracle's time does not depend on the values)."""
+    import oracle
+    import synth
+    H, F, V = 5120, 17408, 248320
+    threads = oracle.max_threads()
+    out = {}
+    for M in Ms:
+        t = {}
+        x_h = synth.integer_activations(91, M, H)
+        x_f = synth.integer_activations(92, M, F)
+        wq, ws = synth.exact_weights(93, H, H)
+        t0 = time.perf_counter()
+        oracle.gemm(wq, ws, np.float32(32.0), x_h, M, H, H, nthreads=threads)
+        t["square"] = time.perf_counter() - t0
+        wg, sg = synth.exact_weights(94, F, H)
+        wu, su = synth.exact_weights(95, F, H)
+        t0 = time.perf_counter()
+        oracle.gate_up_swiglu(wg, sg, np.float32(32.0), wu, su, np.float32(32.0), x_h, M, F, H, nthreads=threads)
+        t["gate_up"] = time.perf_counter() - t0
+        del wg, sg, wu, su
+        wd, sd = synth.exact_weights(96, H, F)
+        t0 = time.perf_counter()
+        oracle.gemm(wd, sd, np.float32(32.0), x_f, M, H, F, nthreads=threads)
+        t["down"] = time.perf_counter() - t0
+        del wd, sd
+        wh, sh = synth.exact_weights(97, V, H)
+        t0 = time.perf_counter()
+        oracle.gemm(wh, sh, np.float32(32.0), x_h, M, V, H, nthreads=threads)
+        t["head"] = time.perf_counter() - t0
+        del wh, sh
+        per_token = layers * (t["gate_up"] + t["down"] + 4 * t["square"]) + t["head"]
+        bytes_token = layers * (2 * weight_bytes(F, H) + weight_bytes(H, F) + 4 * weight_bytes(H, H)) + \
+            weight_bytes(V, H)
+        out[f"M{M}"] = {"s_per_token": round(per_token, 3),
+                        "tokens_per_s": round(1.0 / per_token, 5),
+                        "gbs": round(bytes_token / per_token / 1e9, 4),
+                        "s_per_call": {k: round(v, 4) for k, v in t.items()}}
+        log(f"[bench] tower oracle M={M}: {per_token:.2f} s/token (extrapolated), calls {out[f'M{M}']['s_per_call']}")
+    return dict(kind="oracle", cores=threads, cpu_model=cpu_model(), nproc=os.cpu_count(),
+                method=f"{layers} x (gate/up + SwiGLU + down + 4 square projections) + head, from one "
+                       f"timed oracle call per shape at {threads} threads", **out)
+
+
 def copy_calibration(dev, mib=256, reps=4):
     """A plain device-to-device copy of known size, run under the same PMC
     passes as the GEMV to calibrate FETCH_SIZE / WRITE_SIZE."""
@@ -640,6 +689,8 @@ def main():
     tower = bench_tower(dev, stream) if args.tower else None
     del sq
     cpu = None if args.no_cpu_baseline else cpu_baseline()
+    if tower is not None and not args.no_cpu_baseline:
+        tower["cpu_baseline"] = cpu_baseline_tower()
     line = {
         "metric": "effective weight GB/s (NVFP4 codes + E4M3 scales + g per call / time per call), W4A16 GEMV",
         "value": round(gbs, 2),
