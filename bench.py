@@ -233,7 +233,100 @@ def profile_square(args, dev, stream):
                       "gbs": round(bpc / r["per_call"] / 1e9, 1)}), flush=True)
 
 
+PROFILE_CONFIGS = ("square_M1", "square_M7", "gate_up_M1", "gate_up_M7", "down_M1", "down_M7")
+
+
+def profile_config(args, dev, stream):
+    """Only one configuration's graph replays (for rocprofv3 passes that must
+    see that configuration's dispatches alone): `--steps` replays of its 32-64
+    calls after `--warmup`."""
+    name = args.config
+    kind, m = name.rsplit("_M", 1)
+    M = int(m)
+    if kind == "square":
+        fns, b = square_m_fns(square_setup(dev), M, dev)
+    elif kind == "gate_up":
+        Gs, Us = gate_up_weights(dev)
+        fns, b = gate_up_fns(Gs, Us, M, dev)
+    else:
+        fns, b = down_fns(down_weights(dev), M, dev)
+    graph = capture(fns, stream)
+    with torch_stream(stream):
+        for _ in range(args.warmup):
+            graph.replay()
+    total, per = timed_replays(graph, stream, args.steps)
+    calls = args.steps * len(fns)
+    print(json.dumps({"mode": "profile-config", "config": name, "calls_timed": calls,
+                      "bytes_per_call": b, "us_per_call": round(total / calls * 1e6, 4)}), flush=True)
+
+
+def torch_stream(stream):
+    import torch
+    return torch.cuda.stream(stream)
+
+
 # ---- the metric's configurations ------------------------------------------------
+
+def gate_up_weights(dev):
+    """The gate/up configuration's weights: (gate, up) lists of 32 copies of
+    (wq, ws, g) device tensors each, as [wq copies], [ws copies], [g copies]."""
+    import synth
+    c = synth.CONFIGS["gate_up"]
+    N, K, copies = c["N"], c["K"], c["copies"]
+    log(f"[bench] generating gate/up K={K} 2 x N={N} x{copies} (device quantiser)")
+    G = gpu_weights(c["seed_gate"], N, K, dev)
+    U = gpu_weights(c["seed_up"], N, K, dev)
+    return [replicate(t, copies) for t in G], [replicate(t, copies) for t in U]
+
+
+def down_weights(dev):
+    """The down configuration's weights: [wq copies], [ws copies], [g copies]."""
+    import synth
+    c = synth.CONFIGS["down"]
+    N, K, copies = c["N"], c["K"], c["copies"]
+    log(f"[bench] generating down K={K} N={N} x{copies} (device quantiser)")
+    return [replicate(t, copies) for t in gpu_weights(c["seed_w"], N, K, dev)]
+
+
+def gate_up_fns(Gs, Us, M, dev):
+    """One call per weight copy of gate/up + SwiGLU at M rows, and its bytes."""
+    import torch
+    import block_scaled_fp4_w4a16_amd as w4
+    import synth
+    c = synth.CONFIGS["gate_up"]
+    N, K, copies = c["N"], c["K"], c["copies"]
+    x = to_dev_bf16(synth.activations(c["seed_x"], M, K), dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    work = w4.new_workspace(M, N, K, dev, fused=True)
+    fns = [lambda s, i=i: w4.gemm_gate_up_swiglu(Gs[0][i], Gs[1][i], Gs[2][i], Us[0][i], Us[1][i], Us[2][i],
+                                                 x, y=y, workspace=work, stream=s) for i in range(copies)]
+    return fns, 2 * weight_bytes(N, K)
+
+
+def down_fns(Ds, M, dev):
+    """One call per weight copy of the down projection at M rows, and its bytes."""
+    import torch
+    import block_scaled_fp4_w4a16_amd as w4
+    import synth
+    c = synth.CONFIGS["down"]
+    N, K, copies = c["N"], c["K"], c["copies"]
+    x = to_dev_bf16(synth.swiglu_activations(c["seed_a"], c["seed_b"], M, K), dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    work = w4.new_workspace(M, N, K, dev)
+    fns = [lambda s, i=i: w4.gemm(Ds[0][i], Ds[1][i], Ds[2][i], x, y=y, workspace=work, stream=s)
+           for i in range(copies)]
+    return fns, weight_bytes(N, K)
+
+
+def square_m_fns(sq, M, dev):
+    """One call per weight copy of the square projection at M rows, and its bytes."""
+    import torch
+    import block_scaled_fp4_w4a16_amd as w4
+    import synth
+    x = to_dev_bf16(synth.activations(sq["seed_x"], M, sq["K"]), dev)
+    y = torch.empty((M, sq["N"]), dtype=torch.bfloat16, device=dev)
+    return square_fns(sq, x, y, w4.new_workspace(M, sq["N"], sq["K"], dev)), weight_bytes(sq["N"], sq["K"])
+
 
 def bench_configs(dev, stream, sq, extra=False):
     """Square M = 7; gate/up + SwiGLU M = 1, 7; down M = 1, 7 (with --extra
@@ -242,46 +335,22 @@ def bench_configs(dev, stream, sq, extra=False):
     import block_scaled_fp4_w4a16_amd as w4
     import synth
     out = {}
-    bsq = weight_bytes(sq["N"], sq["K"])
-    x7 = to_dev_bf16(synth.activations(sq["seed_x"], 7, sq["K"]), dev)
-    y7 = torch.empty((7, sq["N"]), dtype=torch.bfloat16, device=dev)
-    out["square_M7"] = time_config(square_fns(sq, x7, y7, w4.new_workspace(7, sq["N"], sq["K"], dev)), stream,
-                                   bsq, replays_per_window=2)
+    fns, b = square_m_fns(sq, 7, dev)
+    out["square_M7"] = time_config(fns, stream, b, replays_per_window=2)
     log(f"[bench] square M=7: {out['square_M7']['us_per_call']} us/call, {out['square_M7']['gbs']} GB/s")
 
-    c = synth.CONFIGS["gate_up"]
-    N, K, copies = c["N"], c["K"], c["copies"]
-    log(f"[bench] generating gate/up K={K} 2 x N={N} x{copies} (device quantiser)")
-    G = gpu_weights(c["seed_gate"], N, K, dev)
-    U = gpu_weights(c["seed_up"], N, K, dev)
-    Gs = [replicate(t, copies) for t in G]
-    Us = [replicate(t, copies) for t in U]
-    del G, U
-    b_gu = 2 * weight_bytes(N, K)
+    Gs, Us = gate_up_weights(dev)
     for M in (1, 7):
-        x = to_dev_bf16(synth.activations(c["seed_x"], M, K), dev)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        work = w4.new_workspace(M, N, K, dev, fused=True)
-        fns = [lambda s, i=i: w4.gemm_gate_up_swiglu(Gs[0][i], Gs[1][i], Gs[2][i], Us[0][i], Us[1][i], Us[2][i],
-                                                     x, y=y, workspace=work, stream=s) for i in range(copies)]
-        out[f"gate_up_M{M}"] = time_config(fns, stream, b_gu)
+        fns, b = gate_up_fns(Gs, Us, M, dev)
+        out[f"gate_up_M{M}"] = time_config(fns, stream, b)
         log(f"[bench] gate/up M={M}: {out[f'gate_up_M{M}']['us_per_call']} us/call, {out[f'gate_up_M{M}']['gbs']} GB/s")
 
-    c = synth.CONFIGS["down"]
-    N, K, copies = c["N"], c["K"], c["copies"]
-    log(f"[bench] generating down K={K} N={N} x{copies} (device quantiser)")
-    D = gpu_weights(c["seed_w"], N, K, dev)
-    Ds = [replicate(t, copies) for t in D]
-    del D
-    b_d = weight_bytes(N, K)
+    Ds = down_weights(dev)
     for M in ((1, 2, 4, 7, 8, 16, 32) if extra else (1, 7)):
-        x = to_dev_bf16(synth.swiglu_activations(c["seed_a"], c["seed_b"], M, K), dev)
-        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        work = w4.new_workspace(M, N, K, dev)
-        fns = [lambda s, i=i: w4.gemm(Ds[0][i], Ds[1][i], Ds[2][i], x, y=y, workspace=work, stream=s)
-               for i in range(copies)]
-        out[f"down_M{M}"] = time_config(fns, stream, b_d)
+        fns, b = down_fns(Ds, M, dev)
+        out[f"down_M{M}"] = time_config(fns, stream, b)
         log(f"[bench] down M={M}: {out[f'down_M{M}']['us_per_call']} us/call, {out[f'down_M{M}']['gbs']} GB/s")
+    N, K, copies = synth.CONFIGS["down"]["N"], synth.CONFIGS["down"]["K"], synth.CONFIGS["down"]["copies"]
 
     if extra:
         # the whole MLP block per call: two launches (graph replay), and eager
@@ -610,6 +679,45 @@ def ingest_pmc(d):
     print(json.dumps(out))
 
 
+TRAFFIC_CONFIGS_FILE = os.path.join(PROFILES, "traffic_configs.json")
+
+
+def ingest_pmc_configs(d):
+    """Calibrated HBM traffic per call of each configuration from rocprofv3
+    --pmc runs under `d`: pmc_<config>_FETCH_SIZE and pmc_<config>_WRITE_SIZE
+    (--mode profile-config --config <config>) and the copy calibration
+    pmc_copy_FETCH_SIZE / pmc_copy_WRITE_SIZE (--mode copy).  Writes
+    traffic_configs.json: per configuration the calibrated bytes per call, the
+    algorithmic bytes and their ratio."""
+    def values(sub, pred):
+        rows = _csv_rows(os.path.join(d, sub), "*counter_collection.csv")
+        return [float(r["Counter_Value"]) for r in rows if pred(r["Kernel_Name"])]
+
+    copy_kib = 256 * 1024
+    factor = {ctr: copy_kib / statistics.median(values(f"pmc_copy_{ctr}", lambda n: "copyBuffer" in n))
+              for ctr in ("FETCH_SIZE", "WRITE_SIZE")}
+    algo = {"square": weight_bytes(5120, 5120), "gate_up": 2 * weight_bytes(17408, 5120),
+            "down": weight_bytes(5120, 17408)}
+    out = {"kernel_source_hash": kernel_source_hash(), "unit": "bytes per call",
+           "copy_factor": {k: round(v, 4) for k, v in factor.items()}, "configs": {}}
+    for name in PROFILE_CONFIGS:
+        if not os.path.isdir(os.path.join(d, f"pmc_{name}_FETCH_SIZE")):
+            continue
+        rec = {}
+        total = 0.0
+        for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+            kib = statistics.median(values(f"pmc_{name}_{ctr}", lambda n: "k_gemm" in n))
+            rec[ctr + "_kib_per_dispatch"] = kib
+            total += kib * factor[ctr] * 1024
+        a = algo[name.rsplit("_M", 1)[0]]
+        rec.update(bytes_per_call=round(total), algorithmic_bytes_per_call=a, ratio=round(total / a, 4))
+        out["configs"][name] = rec
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(TRAFFIC_CONFIGS_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
 def ingest_trace(d):
     """Per-dispatch durations of the matmul kernels from a rocprofv3
     --kernel-trace run of --mode profile-square (there every dispatch of the
@@ -644,15 +752,20 @@ def main():
                     help="skip the achievable-read-bandwidth calibration")
     ap.add_argument("--no-configs", action="store_true",
                     help="only the default workload (no square M=7, gate/up, down)")
-    ap.add_argument("--mode", choices=["bench", "profile-square", "copy", "ingest-pmc", "ingest-trace"],
+    ap.add_argument("--mode", choices=["bench", "profile-square", "profile-config", "copy", "ingest-pmc",
+                                       "ingest-pmc-configs", "ingest-trace"],
                     default="bench",
                     help="profile-square: only the default workload's graph replays (for rocprofv3); "
-                         "copy: the PMC calibration copy; ingest-pmc / ingest-trace: summarise rocprofv3 "
-                         "outputs under --prof-dir")
+                         "profile-config: only --config's graph replays; copy: the PMC calibration copy; "
+                         "ingest-*: summarise rocprofv3 outputs under --prof-dir")
+    ap.add_argument("--config", choices=PROFILE_CONFIGS, default="square_M1")
     ap.add_argument("--prof-dir", default=None)
     args = ap.parse_args()
     if args.mode == "ingest-pmc":
         ingest_pmc(args.prof_dir)
+        return
+    if args.mode == "ingest-pmc-configs":
+        ingest_pmc_configs(args.prof_dir)
         return
     if args.mode == "ingest-trace":
         ingest_trace(args.prof_dir)
@@ -669,6 +782,9 @@ def main():
     stream = torch.cuda.current_stream()
     if args.mode == "copy":
         copy_calibration(dev)
+        return
+    if args.mode == "profile-config":
+        profile_config(args, dev, stream)
         return
     if args.mode == "profile-square":
         profile_square(args, dev, stream)
