@@ -480,14 +480,23 @@ def bench_tower(dev, stream, Ms=(1, 7), layers=64, replays=5):
     return out
 
 
-def calibration(dev, stream, copies, call_bytes=5120 * 5120 // 2 + 5120 * 5120 // 16):
+# call sizes of the configurations, for the call-sized read calibration:
+# (bytes of codes and scales per call, weight copies cycled)
+CALL_SIZES = {"square": (5120 * 5120 // 2 + 5120 * 5120 // 16, 64),
+              "gate_up": (2 * (17408 * 5120 // 2 + 17408 * 5120 // 16), 32),
+              "down": (5120 * 17408 // 2 + 5120 * 17408 // 16, 32)}
+
+
+def calibration(dev, stream, sizes=CALL_SIZES):
     """Achievable HBM read rates, from a plain 128-bit non-temporal streaming
-    read (libw4a16_calib.so, not the matmul library): once on a 4 GiB buffer
-    (32 workgroups of 1024 threads per CU: the fastest launch shape of a sweep
-    on MI355X), and over `copies` buffers of one square call's weight bytes
-    cycled like the weight copies, with the GEMV's grid (one workgroup of 512
-    threads per CU), in a HIP graph like the benchmark.  The second rate
-    includes the same per-call fixed costs."""
+    read (libw4a16_calib.so, not the matmul library, 8 loads in flight per
+    thread): once on a 4 GiB buffer (32 workgroups of 1024 threads per CU: the
+    fastest launch shape of a sweep on MI355X), and for each configuration's
+    call size over as many buffers of that size as the configuration cycles
+    weight copies, one workgroup per CU (the best of 256, 512 and 1024
+    threads), in a HIP graph like the benchmark.  The call-sized rates include
+    the same per-call fixed costs (launch, first-load latency, tail) as the
+    matmul calls, so they are the floor a call of that size can reach."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "block_scaled_fp4_w4a16_amd", "libw4a16_calib.so")
@@ -513,17 +522,25 @@ def calibration(dev, stream, copies, call_bytes=5120 * 5120 // 2 + 5120 * 5120 /
     _, per = timed_replays(g, stream, 10)
     t_big = statistics.median(per)
     del g, big
-    bufs = [torch.ones(call_bytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
-    g = capture([lambda s, i=i: read(bufs[i], call_bytes, cus, 512, s) for i in range(copies)], stream)
-    warm(g, stream)
-    _, per = timed_replays(g, stream, 10)
-    t_call = statistics.median(per) / copies
-    del g, bufs
-    return {"kind": "plain 128-bit non-temporal streaming read (libw4a16_calib.so)",
-            "stream_4gib_gbs": round(big_bytes / t_big / 1e9, 1),
-            "call_sized_bytes": call_bytes, "call_sized_copies": copies,
-            "call_sized_us_per_call": round(t_call * 1e6, 3),
-            "call_sized_gbs": round(call_bytes / t_call / 1e9, 1)}
+    out = {"kind": "plain 128-bit non-temporal streaming read (libw4a16_calib.so)",
+           "stream_4gib_gbs": round(big_bytes / t_big / 1e9, 1), "call_sized": {}}
+    for name, (nbytes, copies) in sizes.items():
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        best = None
+        for block in (256, 512, 1024):
+            g = capture([lambda s, i=i: read(bufs[i], nbytes, cus, block, s) for i in range(copies)], stream)
+            warm(g, stream)
+            _, per = timed_replays(g, stream, 10)
+            t = statistics.median(per) / copies
+            del g
+            if best is None or t < best[0]:
+                best = (t, block)
+        del bufs
+        torch.cuda.empty_cache()
+        out["call_sized"][name] = {"bytes": nbytes, "copies": copies, "block": best[1],
+                                   "us_per_call": round(best[0] * 1e6, 3),
+                                   "gbs": round(nbytes / best[0] / 1e9, 1)}
+    return out
 
 
 def cpu_model():
@@ -797,11 +814,17 @@ def main():
     log(f"[bench] square M=1 (graph replay): {r['per_call']*1e6:.3f} us/call, {gbs:.1f} GB/s; "
         f"windows {[round(u, 3) for u in win_us]}")
     configs = None if args.no_configs else bench_configs(dev, stream, sq, extra=args.extra)
-    cal = None if args.no_calibration else calibration(dev, stream, sq["copies"])
+    cal = None if args.no_calibration else calibration(dev, stream)
     if cal is not None:
         cal["value_frac_of_stream"] = round(gbs / cal["stream_4gib_gbs"], 4)
-        cal["value_frac_of_call_sized"] = round(gbs / cal["call_sized_gbs"], 4)
+        cal["value_frac_of_call_sized"] = round(cal["call_sized"]["square"]["us_per_call"] / (r["per_call"] * 1e6), 4)
         log(f"[bench] calibration: {cal}")
+        # each configuration against a plain read of its call size: time of
+        # that read / time of the call
+        for name, rec in (configs or {}).items():
+            kind = next((k for k in cal["call_sized"] if name.startswith(k + "_M")), None)
+            if kind is not None and "us_per_call" in rec:
+                rec["frac_of_call_sized_read"] = round(cal["call_sized"][kind]["us_per_call"] / rec["us_per_call"], 4)
     tower = bench_tower(dev, stream) if args.tower else None
     del sq
     cpu = None if args.no_cpu_baseline else cpu_baseline()
