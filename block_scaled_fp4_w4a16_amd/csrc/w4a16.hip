@@ -65,6 +65,7 @@ struct Plan {
   size_t lds;  // dynamic LDS bytes per workgroup
   size_t ws;   // workspace bytes (fp32 partials) when S > 1
   int rows_cpl; // > 0: the whole-row VALU kernel for K = 1024 * rows_cpl (S = 1)
+  int xr_cpl;   // > 0: the K-column MFMA kernel for K = 1024 * xr_cpl (S = 1)
 };
 
 // ---- kernel registry ---------------------------------------------------------
@@ -212,13 +213,80 @@ bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
   return true;
 }
 
+// K-column MFMA kernels with x in registers (k_gemm_xr), 3 <= M <= 8 at
+// K = 5120 (CPL = 5), plain and SwiGLU epilogues; other shapes take the MFMA
+// kernel.  (Measured on MI355X against the MFMA kernel, HIP-graph replay:
+// 5120 x 5120 at M = 3, 4, 5, 7, 8: 5.79 / 6.06 / 6.62 / 7.09 / 7.43 us
+// against 7.02 / 7.07 / 7.85 / 7.99 / 8.01; gate/up 2 x 17408 x 5120 at
+// M = 4, 5, 7, 8: 20.9 / 22.4 / 23.3 / 24.2 us against 22.1 / 23.3 / 23.9 /
+// 24.3.)
+struct XrEntry {
+  int M, cpl, epi;
+  const void* fn;
+};
+#define W4A16_XE(MM, F) {MM, 5, F, reinterpret_cast<const void*>(&k_gemm_xr<MM, 5, F>)},
+#define W4A16_XE_ALL(F) \
+  W4A16_XE(3, F) W4A16_XE(4, F) W4A16_XE(5, F) W4A16_XE(6, F) W4A16_XE(7, F) W4A16_XE(8, F)
+const XrEntry kXrKernels[] = {W4A16_XE_ALL(kEpiPlain) W4A16_XE_ALL(kEpiSwiglu)};
+#undef W4A16_XE_ALL
+#undef W4A16_XE
+const void* find_xr_kernel(int M, int cpl, int epi) {
+  for (const XrEntry& e : kXrKernels)
+    if (e.M == M && e.cpl == cpl && e.epi == epi) return e.fn;
+  return nullptr;
+}
+// LDS bytes of k_gemm_xr<M, cpl, ...> for a row block of `rows` rows: one
+// fp32 partial per (quad, weight row, activation row, wave, 16-lane row), with
+// 4 floats of padding per (quad, weight row), as in the kernel
+size_t xr_lds(int M, int cpl, bool fused, long long rows) {
+  const size_t quads = (size_t)((rows + 3) / 4) * (fused ? 2 : 1);
+  return quads * 4 * ((size_t)M * 4 * (size_t)cpl + 4) * sizeof(float);
+}
+
+// Plan for the K-column kernel, or false if it does not apply: one row block
+// per CU, or 2, 4, ... times as many while a block's partials outgrow LDS.
+bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
+  if (M < 3 || M > 8 || epi == kEpiArgmax || K % 1024 != 0) return false;
+#ifdef W4A16_TUNING
+  if (g_override.enable) return false;
+#endif
+  const int cpl = K / 1024;
+  if (!find_xr_kernel(M, cpl, epi)) return false;
+  const bool fused = epi == kEpiSwiglu;
+  long long nrb = cu_count();
+  if (nrb > N) nrb = N;
+  if (nrb < 1) nrb = 1;
+  while (xr_lds(M, cpl, fused, N / nrb + (N % nrb > 0)) > kMaxLds) {
+    if (nrb >= N) return false;
+    nrb = 2 * nrb < N ? 2 * nrb : N;
+  }
+  pl = Plan{};
+  pl.mfma = true;
+  pl.lr = 1;
+  pl.W = cpl;
+  pl.LB = 64 * cpl;
+  pl.nrb = (int)nrb;
+  pl.S = 1;
+  pl.rq = N / (int)nrb;
+  pl.rr = N % (int)nrb;
+  pl.lds = xr_lds(M, cpl, fused, pl.rq + (pl.rr > 0));
+  pl.ws = 0;
+  pl.xr_cpl = cpl;
+  return true;
+}
+
 // Kernel selection is a pure function of (M, N, K, epilogue) and the device's
-// compute-unit count.  rows_ok: whether the whole-row kernel may be chosen
-// (the persistent MLP kernel runs the general kernels' bodies only).
-Plan plan_gemm(int M, int N, int K, int epi, bool rows_ok = true) {
+// compute-unit count.  rows_ok, xr_ok: whether the whole-row and the K-column
+// kernels may be chosen.  The persistent MLP kernel runs the general kernels'
+// bodies only; the MLP block's two-launch path may take the whole-row kernel
+// (its sums are the VALU kernel's, bit for bit) but not the K-column kernel
+// (whose sums are added in another order than the MFMA kernel's), so that
+// both paths of the block give the same bits.
+Plan plan_gemm(int M, int N, int K, int epi, bool rows_ok = true, bool xr_ok = true) {
   {
     Plan r;
     if (rows_ok && plan_rows(M, N, K, epi, r)) return r;
+    if (xr_ok && plan_xr(M, N, K, epi, r)) return r;
   }
   const bool fused = epi == kEpiSwiglu;
   Plan pl{};
@@ -372,6 +440,11 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t
 }
 
 hipError_t dispatch(const Plan& pl, int epi, hipStream_t s, const MatArgs& a) {
+  if (pl.xr_cpl > 0) {
+    const void* fn = find_xr_kernel(a.M, pl.xr_cpl, epi);
+    if (!fn || pl.W != pl.xr_cpl || a.K != 1024 * pl.xr_cpl) return hipErrorInvalidConfiguration;
+    return launch(fn, dim3((unsigned)pl.nrb), dim3((unsigned)(pl.W * 64)), pl.lds, s, a);
+  }
   if (pl.rows_cpl > 0) {
     const void* fn = find_rows_kernel(a.M, pl.rows_cpl, epi);
     if (!fn || pl.W < 4 || pl.W * 64 > pl.LB || a.K != 1024 * pl.rows_cpl)
@@ -471,8 +544,8 @@ MlpPlan plan_mlp(int M, int H, int F) {
   MlpPlan mp{};
   // the general kernels' plans: the persistent kernel runs their bodies, and
   // their workspace covers every variant (the whole-row kernel needs none)
-  mp.p1 = plan_gemm(M, F, H, kEpiSwiglu, false);
-  mp.p2 = plan_gemm(M, H, F, kEpiPlain, false);
+  mp.p1 = plan_gemm(M, F, H, kEpiSwiglu, false, false);
+  mp.p2 = plan_gemm(M, H, F, kEpiPlain, false, false);
   if (mp.p1.S == 0 || mp.p2.S == 0) return MlpPlan{};
   const size_t h_bytes = align256((size_t)M * F * 2);
   const size_t w1 = mp.p1.ws > 0 ? align256(mp.p1.ws - kCounterBytes) : 0;
@@ -565,8 +638,10 @@ w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace
     if (e == hipSuccess) return W4A16_OK;
     (void)hipGetLastError();  // clear the refused launch's error
   }
-  // two launches: each phase takes its own best plan
-  const Plan q1 = plan_gemm(M, F, H, kEpiSwiglu), q2 = plan_gemm(M, H, F, kEpiPlain);
+  // two launches: each phase takes its own best plan among the kernels whose
+  // sums match the persistent kernel's bit for bit
+  const Plan q1 = plan_gemm(M, F, H, kEpiSwiglu, true, false),
+             q2 = plan_gemm(M, H, F, kEpiPlain, true, false);
   if (q1.S == 0 || q2.S == 0 || q1.lds > kMaxLds || q2.lds > kMaxLds || q1.ws > mp.p1.ws ||
       q2.ws > mp.p2.ws)
     return W4A16_ERR_UNSUPPORTED;

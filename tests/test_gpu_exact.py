@@ -158,14 +158,39 @@ def test_whole_row_kernel_fused_ragged_n_exact(M, N):
     fused_exact(M, N, 5120, 1700 + 7 * M + N, ctx="rows fused")
 
 
+# ---- the K-column kernel (K = 5120, 3 <= M <= 8): every M, row-block edges ----
+
+@pytest.mark.parametrize("M", [3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N", [1, 3, 257, 1029, 5120])
+def test_k_column_kernel_every_m_exact(M, N):
+    """Each M is its own instantiation (one or two passes of 4 activation rows,
+    rows >= M skipped at compile time); N below and past the CU count, blocks
+    without rows and a ragged last quad."""
+    gemm_exact(M, N, 5120, 1800 + 11 * M + N, "mant" if (M + N) % 2 else "pow2", ctx="k-column")
+
+
+@pytest.mark.parametrize("M", [3, 5, 8])
+@pytest.mark.parametrize("N", [1, 1030, 17408])
+def test_k_column_kernel_fused_exact(M, N):
+    """Fused quads alternate gate and up rows; the epilogue pairs them."""
+    fused_exact(M, N, 5120, 1900 + 11 * M + N, ctx="k-column fused")
+
+
+def test_k_column_kernel_many_row_blocks_exact():
+    """N so large that one row block per CU would park more partials than
+    the LDS holds: the planner doubles the row blocks (512 here)."""
+    gemm_exact(8, 70000, 5120, 1950, ctx="k-column 70000 rows")
+    fused_exact(7, 40000, 5120, 1960, ctx="k-column fused 40000 rows")
+
+
 # ---- one-hot sweep: every 32-input chunk position of K = 5120 -----------------
 
-@pytest.mark.parametrize("M", [2, 8])
+@pytest.mark.parametrize("M", [2, 8, 16])
 def test_one_hot_every_chunk_position(M):
     """Row m of call i is e_k with k = 32c + (7c mod 32) + ... for chunk c =
-    i*M + m: y[m][n] = bf16(W[n][k]) exactly.  M = 2 runs the VALU kernel,
-    M = 8 the MFMA kernel; together they touch all 160 chunks twice, at two
-    offsets inside each chunk."""
+    i*M + m: y[m][n] = bf16(W[n][k]) exactly.  M = 2 runs the whole-row VALU
+    kernel, M = 8 the K-column kernel, M = 16 the MFMA kernel; each touches
+    all 160 chunks twice, at two offsets inside each chunk."""
     N, K = 2048, 5120
     wq, ws = synth.exact_weights(1300, N, K, "mant")
     g = np.float32(2.0 ** 6)
