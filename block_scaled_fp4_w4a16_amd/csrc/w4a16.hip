@@ -236,11 +236,13 @@ const void* find_xr_kernel(int M, int cpl, int epi) {
   return nullptr;
 }
 // LDS bytes of k_gemm_xr<M, cpl, ...> for a row block of `rows` rows: one
-// fp32 partial per (quad, weight row, activation row, wave, 16-lane row), with
-// 4 floats of padding per (quad, weight row), as in the kernel
+// fp32 partial per (quad, weight row, activation row, wave, 16-lane row), the
+// floats per (quad, weight row) padded to 4 mod 8, as in the kernel
 size_t xr_lds(int M, int cpl, bool fused, long long rows) {
   const size_t quads = (size_t)((rows + 3) / 4) * (fused ? 2 : 1);
-  return quads * 4 * ((size_t)M * 4 * (size_t)cpl + 4) * sizeof(float);
+  size_t js = (size_t)M * 4 * (size_t)cpl;
+  js += js % 8 == 0 ? 4 : 0;
+  return quads * 4 * js * sizeof(float);
 }
 
 // Plan for the K-column kernel, or false if it does not apply: one row block

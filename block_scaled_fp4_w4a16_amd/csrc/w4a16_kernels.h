@@ -1078,7 +1078,9 @@ __global__ void __launch_bounds__(64 * CPL) k_gemm_xr(MatArgs a) {
   constexpr int W = CPL;         // waves: (2 CPL columns) / KJ
   constexpr int G = 2;           // quads per task
   constexpr int WR = 4 * W;      // partials per (quad, weight row, activation row)
-  constexpr int JS = M * WR + 4; // LDS floats per (quad, weight row); the pad spreads banks
+  // LDS floats per (quad, weight row), = 4 mod 8: the 16 writer lanes (4 weight
+  // rows x 4 lane rows) of a partial then hit 16 distinct banks
+  constexpr int JS = M * WR + ((M * WR) % 8 == 0 ? 4 : 0);
   static_assert(M >= 3 && M <= 8, "the K-column kernel serves 3 <= M <= 8");
   extern __shared__ float red[];
   const int tid = threadIdx.x, lane = tid & 63;
