@@ -246,7 +246,10 @@ size_t xr_lds(int M, int cpl, bool fused, long long rows) {
 }
 
 // Plan for the K-column kernel, or false if it does not apply: one row block
-// per CU, or 2, 4, ... times as many while a block's partials outgrow LDS.
+// per CU, whose partials must fit in LDS (N up to ~63 000 plain, ~31 000
+// fused at M = 8).  More blocks would each load x again: on the 5120 ->
+// 248 320 head at M = 7, 1024 blocks took 154.6 us against 145.6 for the MFMA
+// kernel (measured on MI355X), so larger N takes the MFMA kernel.
 bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
   if (M < 3 || M > 8 || epi == kEpiArgmax || K % 1024 != 0) return false;
 #ifdef W4A16_TUNING
@@ -258,10 +261,7 @@ bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
   long long nrb = cu_count();
   if (nrb > N) nrb = N;
   if (nrb < 1) nrb = 1;
-  while (xr_lds(M, cpl, fused, N / nrb + (N % nrb > 0)) > kMaxLds) {
-    if (nrb >= N) return false;
-    nrb = 2 * nrb < N ? 2 * nrb : N;
-  }
+  if (xr_lds(M, cpl, fused, N / nrb + (N % nrb > 0)) > kMaxLds) return false;
   pl = Plan{};
   pl.mfma = true;
   pl.lr = 1;

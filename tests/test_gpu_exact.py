@@ -176,11 +176,16 @@ def test_k_column_kernel_fused_exact(M, N):
     fused_exact(M, N, 5120, 1900 + 11 * M + N, ctx="k-column fused")
 
 
-def test_k_column_kernel_many_row_blocks_exact():
-    """N so large that one row block per CU would park more partials than
-    the LDS holds: the planner doubles the row blocks (512 here)."""
-    gemm_exact(8, 70000, 5120, 1950, ctx="k-column 70000 rows")
-    fused_exact(7, 40000, 5120, 1960, ctx="k-column fused 40000 rows")
+@pytest.mark.parametrize("M,N,fused", [(8, 63488, False), (8, 63489, False), (7, 35000, True),
+                                         (7, 40000, True)])
+def test_k_column_kernel_lds_limit_exact(M, N, fused):
+    """Either side of the largest N whose row blocks (one per CU) fit their
+    partials in LDS: 63 488 rows plain at M = 8 (248 per block) still run the
+    K-column kernel, 63 489 the MFMA kernel; likewise fused at 35 000 / 40 000."""
+    if fused:
+        fused_exact(M, N, 5120, 1960 + N % 97, ctx=f"k-column limit fused N={N}")
+    else:
+        gemm_exact(M, N, 5120, 1950 + N % 97, ctx=f"k-column limit N={N}")
 
 
 # ---- one-hot sweep: every 32-input chunk position of K = 5120 -----------------
