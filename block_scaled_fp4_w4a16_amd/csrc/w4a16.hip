@@ -467,8 +467,34 @@ w4a16_status_t check_shape(int M, int N, int K) {
   return W4A16_OK;
 }
 
+// Wide M: whether a call runs as two launches over activation rows [0, m1)
+// and [m1, M), and m1 (a multiple of 4, at most 16; 0 for one launch).  Taken
+// where the one-launch plan splits K so finely that its partial sums and
+// their finish cost more than reading the weights twice: plain calls whose
+// plan needs 16 or more K-slices, SwiGLU calls above 20 rows (two partial
+// sets per slice).  Measured on MI355X (HIP-graph replay): the down
+// projection 5120 x 17408 at M = 32 in 75.0 us as one launch (16 slices),
+// 2 x 24.2 as two of 16 rows; gate/up 2 x 17408 x 5120 at M = 24 / 28 / 32 in
+// 79.4 / 92.7 / 105.9 us as one, 2 x 28.7 / 42.1 + 28.7 / 2 x 42.1 as two;
+// one launch stays faster for the square 5120 x 5120 at every M and for the
+// down projection up to M = 28 (8 slices).  Not for the argmax epilogue
+// (whose candidates span all rows) or the MLP block (whose two paths must
+// give the same bits).
+int split_rows(int M, int N, int K, int epi) {
+  if (M <= 16 || epi == kEpiArgmax) return 0;
+  int m1 = (M / 2 + 3) / 4 * 4;
+  if (m1 > 16) m1 = 16;
+  if (epi == kEpiSwiglu) return M > 20 ? m1 : 0;
+  return plan_gemm(M, N, K, epi).S >= 16 ? m1 : 0;
+}
+
 size_t workspace_bytes_for(int M, int N, int K, int epi) {
   if (check_shape(M, N, K) != W4A16_OK) return 0;
+  const int m1 = split_rows(M, N, K, epi);
+  if (m1 > 0) {
+    const size_t w1 = plan_gemm(m1, N, K, epi).ws, w2 = plan_gemm(M - m1, N, K, epi).ws;
+    return w1 > w2 ? w1 : w2;
+  }
   return plan_gemm(M, N, K, epi).ws;
 }
 
@@ -489,8 +515,8 @@ void prepare(MatArgs& a, const Plan& pl, int* cnt, float* part) {
   a.cand = part;
 }
 
-w4a16_status_t run_matmul(MatArgs a, int epi, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
+w4a16_status_t run_matmul_one(MatArgs a, int epi, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
   const Plan pl = plan_gemm(a.M, a.N, a.K, epi);
   if (pl.S == 0 || pl.lds > kMaxLds) return W4A16_ERR_UNSUPPORTED;
   if (workspace_bytes < pl.ws || (pl.ws > 0 && workspace == nullptr))
@@ -502,6 +528,22 @@ w4a16_status_t run_matmul(MatArgs a, int epi, void* workspace, size_t workspace_
   if (epi == kEpiArgmax && pl.S > 1) a.cand = a.part + (size_t)pl.S * (size_t)a.M * (size_t)a.N;
   const hipError_t e = dispatch(pl, epi, stream, a);
   return e == hipSuccess ? W4A16_OK : W4A16_ERR_LAUNCH;
+}
+
+// One launch, or two over row ranges of x and y (split_rows); the second
+// reuses the workspace after the first on the same stream (every launch
+// leaves its arrival counters at zero).
+w4a16_status_t run_matmul(MatArgs a, int epi, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  const int m1 = split_rows(a.M, a.N, a.K, epi);
+  if (m1 == 0) return run_matmul_one(a, epi, workspace, workspace_bytes, stream);
+  MatArgs a1 = a, a2 = a;
+  a1.M = m1;
+  a2.M = a.M - m1;
+  a2.x = a.x + (size_t)m1 * a.K;
+  a2.y = a.y + (size_t)m1 * a.N;
+  const w4a16_status_t st = run_matmul_one(a1, epi, workspace, workspace_bytes, stream);
+  return st != W4A16_OK ? st : run_matmul_one(a2, epi, workspace, workspace_bytes, stream);
 }
 
 // ---- MLP block: gate/up + SwiGLU, then down ------------------------------------
@@ -742,7 +784,8 @@ w4a16_status_t w4a16_gemm_noalloc(const uint8_t* wq, const uint8_t* ws, const fl
       !aligned(y, 4))
     return W4A16_ERR_UNSUPPORTED;
   const Plan pl = plan_gemm(M, N, K, kEpiPlain);
-  if (pl.S == 0 || pl.lds > kMaxLds || pl.ws > kNoallocScratchBytes) return W4A16_ERR_UNSUPPORTED;
+  if (pl.S == 0 || pl.lds > kMaxLds || workspace_bytes_for(M, N, K, kEpiPlain) > kNoallocScratchBytes)
+    return W4A16_ERR_UNSUPPORTED;
   void* work = nullptr;
   st = noalloc_scratch(stream, &work);
   if (st != W4A16_OK) return st;
