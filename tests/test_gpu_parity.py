@@ -223,6 +223,36 @@ def test_nan_scale_propagates_to_its_row_only():
         assert not np.isnan(np.delete(y, 17, axis=1)).any()
 
 
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 8])
+def test_uniform_random_bytes_at_k5120(M):
+    """The K = 5120 kernels (whole-row for M <= 2, K-column for 3 <= M <= 8) on
+    every code byte and random finite scales of both signs."""
+    N, K = 300, 5120
+    wq = synth.random_bytes(21, (N, K // 2))
+    ws = synth.random_bytes(22, (N, K // 16)) & np.uint8(0x77)
+    ws |= synth.random_bytes(23, (N, K // 16)) & np.uint8(0x80)
+    check_gemm(wq, ws, np.float32(1234.5), synth.activations(24 + M, M, K), M, N, K, "random bytes K=5120")
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_nan_scale_propagates_to_its_row_only_at_k5120(M):
+    """A NaN block scale (E4M3 0x7F) in one row reaches that row's outputs
+    only, through the K = 5120 kernels' lane, block and wave reductions."""
+    N, K = 300, 5120
+    wq, ws, g = weights(25, N, K)
+    ws = ws.copy()
+    ws[130, 201] = 0x7F
+    y = run_gemm(wq, ws, g, synth.activations(26, M, K), M, N, K)
+    assert np.isnan(y[:, 130]).all()
+    assert not np.isnan(np.delete(y, 130, axis=1)).any()
+    wu, su, gu = weights(27, N, K)
+    yf = w4.gemm_gate_up_swiglu(d_u8(wq), d_u8(ws), d_g(g), d_u8(wu), d_u8(su), d_g(gu),
+                                d_bf16(synth.activations(26, M, K)))
+    yf = h_bf16(yf)
+    assert np.isnan(yf[:, 130]).all()
+    assert not np.isnan(np.delete(yf, 130, axis=1)).any()
+
+
 def test_zero_weights_give_zero():
     for M in (1, 5):
         N, K = 50, 256
