@@ -471,8 +471,8 @@ w4a16_status_t check_shape(int M, int N, int K) {
 // and [m1, M), and m1 (a multiple of 4, at most 16; 0 for one launch).  Taken
 // where the one-launch plan splits K so finely that its partial sums and
 // their finish cost more than reading the weights twice: plain calls whose
-// plan needs 16 or more K-slices, SwiGLU calls above 20 rows (two partial
-// sets per slice).  Measured on MI355X (HIP-graph replay): the down
+// plan needs 16 or more K-slices, SwiGLU calls whose plan needs 4 or more
+// (two partial sets per slice).  Measured on MI355X (HIP-graph replay): the down
 // projection 5120 x 17408 at M = 32 in 75.0 us as one launch (16 slices),
 // 2 x 24.2 as two of 16 rows; gate/up 2 x 17408 x 5120 at M = 24 / 28 / 32 in
 // 79.4 / 92.7 / 105.9 us as one, 2 x 28.7 / 42.1 + 28.7 / 2 x 42.1 as two;
@@ -484,8 +484,7 @@ int split_rows(int M, int N, int K, int epi) {
   if (M <= 16 || epi == kEpiArgmax) return 0;
   int m1 = (M / 2 + 3) / 4 * 4;
   if (m1 > 16) m1 = 16;
-  if (epi == kEpiSwiglu) return M > 20 ? m1 : 0;
-  return plan_gemm(M, N, K, epi).S >= 16 ? m1 : 0;
+  return plan_gemm(M, N, K, epi).S >= (epi == kEpiSwiglu ? 4 : 16) ? m1 : 0;
 }
 
 size_t workspace_bytes_for(int M, int N, int K, int epi) {
