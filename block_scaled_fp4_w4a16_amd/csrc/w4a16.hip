@@ -237,12 +237,16 @@ const void* find_xr_kernel(int M, int cpl, int epi) {
 }
 // LDS bytes of k_gemm_xr<M, cpl, ...> for a row block of `rows` rows: one
 // fp32 partial per (quad, weight row, activation row, wave, 16-lane row), the
-// floats per (quad, weight row) padded to 4 mod 8, as in the kernel
+// floats per (quad, weight row) padded to 4 mod 8, as in the kernel; at least
+// the area the waves first stage their x in (2 columns x P passes x 4 units x
+// 64 lanes x 16 bytes per wave)
 size_t xr_lds(int M, int cpl, bool fused, long long rows) {
   const size_t quads = (size_t)((rows + 3) / 4) * (fused ? 2 : 1);
   size_t js = (size_t)M * 4 * (size_t)cpl;
   js += js % 8 == 0 ? 4 : 0;
-  return quads * 4 * js * sizeof(float);
+  const size_t partials = quads * 4 * js * sizeof(float);
+  const size_t x_stage = (size_t)cpl * 2 * ((M + 3) / 4) * 4 * 64 * 16;
+  return partials > x_stage ? partials : x_stage;
 }
 
 // Plan for the K-column kernel, or false if it does not apply: one row block
