@@ -216,66 +216,78 @@ bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
 // K-column MFMA kernels with x in registers (k_gemm_xr), 3 <= M <= 8 at
 // K = 5120 (CPL = 5), plain and SwiGLU epilogues; other shapes take the MFMA
 // kernel.  (Measured on MI355X against the MFMA kernel, HIP-graph replay:
-// 5120 x 5120 at M = 3, 4, 5, 7, 8: 5.79 / 6.06 / 6.62 / 7.09 / 7.43 us
+// 5120 x 5120 at M = 3, 4, 5, 7, 8: 5.55 / 5.61 / 6.43 / 6.60 / 6.68 us
 // against 7.02 / 7.07 / 7.85 / 7.99 / 8.01; gate/up 2 x 17408 x 5120 at
-// M = 4, 5, 7, 8: 20.9 / 22.4 / 23.3 / 24.2 us against 22.1 / 23.3 / 23.9 /
+// M = 4, 5, 7, 8: 20.2 / 21.2 / 21.6 / 21.8 us against 22.1 / 23.3 / 23.9 /
 // 24.3.)
 struct XrEntry {
-  int M, cpl, epi;
+  int M, cpl, epi, W;
   const void* fn;
 };
-#define W4A16_XE(MM, F) {MM, 5, F, reinterpret_cast<const void*>(&k_gemm_xr<MM, 5, F>)},
-#define W4A16_XE_ALL(F) \
-  W4A16_XE(3, F) W4A16_XE(4, F) W4A16_XE(5, F) W4A16_XE(6, F) W4A16_XE(7, F) W4A16_XE(8, F)
-const XrEntry kXrKernels[] = {W4A16_XE_ALL(kEpiPlain) W4A16_XE_ALL(kEpiSwiglu)};
+#define W4A16_XE(MM, F, WW) {MM, 5, F, WW, reinterpret_cast<const void*>(&k_gemm_xr<MM, 5, F, WW>)},
+#define W4A16_XE_P2(F, WW) W4A16_XE(5, F, WW) W4A16_XE(6, F, WW) W4A16_XE(7, F, WW) W4A16_XE(8, F, WW)
+#define W4A16_XE_ALL(F, WW) W4A16_XE(3, F, WW) W4A16_XE(4, F, WW) W4A16_XE_P2(F, WW)
+const XrEntry kXrKernels[] = {W4A16_XE_ALL(kEpiPlain, 5) W4A16_XE_ALL(kEpiSwiglu, 5)
+                              W4A16_XE_P2(kEpiPlain, 8) W4A16_XE_P2(kEpiSwiglu, 8)};
 #undef W4A16_XE_ALL
+#undef W4A16_XE_P2
 #undef W4A16_XE
-const void* find_xr_kernel(int M, int cpl, int epi) {
+const void* find_xr_kernel(int M, int cpl, int epi, int W) {
   for (const XrEntry& e : kXrKernels)
-    if (e.M == M && e.cpl == cpl && e.epi == epi) return e.fn;
+    if (e.M == M && e.cpl == cpl && e.epi == epi && e.W == W) return e.fn;
   return nullptr;
 }
-// LDS bytes of k_gemm_xr<M, cpl, ...> for a row block of `rows` rows: one
-// fp32 partial per (quad, weight row, activation row, wave, 16-lane row), the
+// LDS bytes of k_gemm_xr<M, ..., W> for a row block of `rows` rows: one fp32
+// partial per (quad, weight row, activation row, wave, 16-lane row), the
 // floats per (quad, weight row) padded to 4 mod 8, as in the kernel; at least
-// the area the waves first stage their x in (2 columns x P passes x 4 units x
-// 64 lanes x 16 bytes per wave)
-size_t xr_lds(int M, int cpl, bool fused, long long rows) {
+// the area the waves first stage their x in (up to 2 columns x P passes x 4
+// units x 64 lanes x 16 bytes per wave)
+size_t xr_lds(int M, bool fused, long long rows, int W) {
   const size_t quads = (size_t)((rows + 3) / 4) * (fused ? 2 : 1);
-  size_t js = (size_t)M * 4 * (size_t)cpl;
+  size_t js = (size_t)M * 4 * (size_t)W;
   js += js % 8 == 0 ? 4 : 0;
   const size_t partials = quads * 4 * js * sizeof(float);
-  const size_t x_stage = (size_t)cpl * 2 * ((M + 3) / 4) * 4 * 64 * 16;
+  const size_t x_stage = (size_t)W * 2 * ((M + 3) / 4) * 4 * 64 * 16;
   return partials > x_stage ? partials : x_stage;
 }
 
 // Plan for the K-column kernel, or false if it does not apply: one row block
 // per CU, whose partials must fit in LDS (N up to ~63 000 plain, ~31 000
-// fused at M = 8).  More blocks would each load x again: on the 5120 ->
+// fused at M = 8, with 5 waves).  More blocks would each load x again: on the 5120 ->
 // 248 320 head at M = 7, 1024 blocks took 154.6 us against 145.6 for the MFMA
-// kernel (measured on MI355X), so larger N takes the MFMA kernel.
+// kernel (measured on MI355X), so larger N takes the MFMA kernel.  Waves:
+// 2 CPL / 2 (two columns each), except 8 for M >= 5 once a block has 16 or
+// more row quads (the first two columns to some waves, one to the rest; two
+// waves per SIMD; 5 again where 8 waves' partials would not fit): measured
+// at M = 7, the square (5 quads per block) 6.55 us with 5 waves, 6.69 with 8;
+// gate/up (34 quads) 22.5 with 5, 21.6 with 8; at M = 3 gate/up 20.1 with 5,
+// 20.3 with 8.
 bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
   if (M < 3 || M > 8 || epi == kEpiArgmax || K % 1024 != 0) return false;
 #ifdef W4A16_TUNING
   if (g_override.enable) return false;
 #endif
   const int cpl = K / 1024;
-  if (!find_xr_kernel(M, cpl, epi)) return false;
   const bool fused = epi == kEpiSwiglu;
   long long nrb = cu_count();
   if (nrb > N) nrb = N;
   if (nrb < 1) nrb = 1;
-  if (xr_lds(M, cpl, fused, N / nrb + (N % nrb > 0)) > kMaxLds) return false;
+  const long long rows = N / nrb + (N % nrb > 0);
+  const long long quads = (rows + 3) / 4 * (fused ? 2 : 1);
+  int W = quads >= 16 && M >= 5 ? 8 : cpl;
+  if (W != cpl && xr_lds(M, fused, rows, W) > kMaxLds) W = cpl;  // fewer partials per quad
+  if (!find_xr_kernel(M, cpl, epi, W)) return false;
+  if (xr_lds(M, fused, rows, W) > kMaxLds) return false;
   pl = Plan{};
   pl.mfma = true;
   pl.lr = 1;
-  pl.W = cpl;
-  pl.LB = 64 * cpl;
+  pl.W = W;
+  pl.LB = 64 * W;
   pl.nrb = (int)nrb;
   pl.S = 1;
   pl.rq = N / (int)nrb;
   pl.rr = N % (int)nrb;
-  pl.lds = xr_lds(M, cpl, fused, pl.rq + (pl.rr > 0));
+  pl.lds = xr_lds(M, fused, pl.rq + (pl.rr > 0), W);
   pl.ws = 0;
   pl.xr_cpl = cpl;
   return true;
@@ -447,8 +459,8 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t
 
 hipError_t dispatch(const Plan& pl, int epi, hipStream_t s, const MatArgs& a) {
   if (pl.xr_cpl > 0) {
-    const void* fn = find_xr_kernel(a.M, pl.xr_cpl, epi);
-    if (!fn || pl.W != pl.xr_cpl || a.K != 1024 * pl.xr_cpl) return hipErrorInvalidConfiguration;
+    const void* fn = find_xr_kernel(a.M, pl.xr_cpl, epi, pl.W);
+    if (!fn || pl.W * 64 != pl.LB || a.K != 1024 * pl.xr_cpl) return hipErrorInvalidConfiguration;
     return launch(fn, dim3((unsigned)pl.nrb), dim3((unsigned)(pl.W * 64)), pl.lds, s, a);
   }
   if (pl.rows_cpl > 0) {

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace w4a16 {
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
@@ -1053,29 +1055,32 @@ __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows
 // The 4x4x4 block product of the MFMA kernel below (block beta = one chunk
 // column, its 4 columns = 4 weight rows, its 4 rows = activation rows; P
 // passes of 4 activation rows), with the work split over K instead of rows:
-// the 2 CPL columns of 16 chunks go two to a wave (CPL waves) and every wave
-// walks every row quad of the workgroup's row block.  A wave therefore holds
-// its slice of x (its two columns of M rows) in VGPRs for the whole call,
-// loaded once from memory: no LDS staging of x, no barrier before the first
-// product, no LDS reads of x per step (the MFMA kernel reads 8 bytes of x
-// from LDS per weight byte at M = 7).  What crosses waves is one partial sum
-// per (quad, weight row, activation row, wave, 16-lane row): the quad's 16
-// blocks are summed in registers (DPP within 16-lane rows) and parked in
-// LDS, and after the loop each output adds its 4 CPL partials in a fixed
-// order.  Fused: quad 2i holds gate rows 4i..4i+3, quad 2i+1 the same up rows.
-// A task is two quads; two tasks are in registers, the next one's loads
-// issued before the current one is computed (the whole-row kernel's loop).
-// Measured on MI355X (HIP-graph replay, 5120 x 5120, 64 cycled copies):
-// 7.09 us at M = 7 against 7.99 for the MFMA kernel, 6.06 against 7.07 at
-// M = 4; gate/up 2 x 17408 x 5120 at M = 7: 23.3 against 23.9 us.
+// the 2 CPL columns of 16 chunks are shared out one or two to a wave (W
+// waves: 2 CPL / 2 of two columns each, or more waves of which the first
+// 2 CPL - W own two and the rest one) and every wave walks every row quad of
+// the workgroup's row block.  A wave therefore holds its slice of x (its
+// columns of M rows) in VGPRs for the whole call, loaded once from memory:
+// no per-step LDS reads of x (the MFMA kernel reads 8 bytes of x from LDS
+// per weight byte at M = 7).  What crosses waves is one partial sum per
+// (quad, weight row, activation row, wave, 16-lane row): the quad's 16 blocks
+// are summed in registers (DPP within 16-lane rows) and parked in LDS, and
+// after the loop each output adds its 4 W partials in a fixed order.  Fused:
+// quad 2i holds gate rows 4i..4i+3, quad 2i+1 the same up rows.  A task is
+// two quads; two tasks are in registers, the next one's loads issued before
+// the current one is computed (the whole-row kernel's loop).
+// Measured on MI355X (HIP-graph replay, 64 / 32 cycled copies): 5120 x 5120
+// at M = 7 in 6.55 us with 5 waves (6.69 with 8) against 7.99 for the MFMA
+// kernel; gate/up 2 x 17408 x 5120 at M = 7 in 21.6 us with 8 waves (22.5
+// with 5) against 23.9.
 // ---------------------------------------------------------------------------
-template <int M, int CPL, int EPI>
-__global__ void __launch_bounds__(64 * CPL) k_gemm_xr(MatArgs a) {
+template <int M, int CPL, int EPI, int W>
+__global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   constexpr bool FUSED = EPI == kEpiSwiglu;
   constexpr int P = (M + 3) / 4;
   constexpr int K = 1024 * CPL;
-  constexpr int KJ = 2;          // chunk columns per wave
-  constexpr int W = CPL;         // waves: (2 CPL columns) / KJ
+  constexpr int JT = 2 * CPL;    // chunk columns of 16 chunks
+  constexpr int N2 = JT - W;     // waves 0..N2-1 own two columns, the rest one
+  static_assert(W <= JT && JT <= 2 * W, "every wave owns one or two columns");
   constexpr int G = 2;           // quads per task
   constexpr int WR = 4 * W;      // partials per (quad, weight row, activation row)
   // LDS floats per (quad, weight row), = 4 mod 8: the 16 writer lanes (4 weight
@@ -1095,173 +1100,189 @@ __global__ void __launch_bounds__(64 * CPL) k_gemm_xr(MatArgs a) {
   const int beta = lane >> 2, j = lane & 3;
   const int shp = (beta & 1) * 16;  // this lane's chunk's scale pair in its scale dword
 
-  // x: lane (beta, j) holds activation rows 4 pp + j of chunk beta + 16 c for
-  // the wave's columns c = KJ wv + kj, as 16-byte units u = 0..3.  Loaded as
-  // one contiguous 1 KB row span per instruction (lane l: bytes 16 l.., i.e.
-  // unit l & 3 of chunk l >> 2 of row 4 pp + u in xv[..][u]) and then
-  // transposed within each quad of lanes through LDS (below).  Measured at
-  // M = 7 on the square: loading each lane's own units directly (16 bytes
-  // per lane at a 64-byte stride) 7.11 us per call, contiguous loads with a
-  // DPP transpose 6.70, with the LDS transpose 6.53.  Rows >= M lie past the
-  // buffer's records and read as zero.
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.x), (short)0, M * K * 2, kBufferWord3);
-  uint4 xv[KJ][P][4];
-#pragma unroll
-  for (int kj = 0; kj < KJ; ++kj)
-#pragma unroll
-    for (int pp = 0; pp < P; ++pp)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int off = (4 * pp + u) * (K * 2) + 16 * (KJ * wv + kj) * 64 + 16 * lane;
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
-        xv[kj][pp][u] = make_uint4(v.x, v.y, v.z, v.w);
-      }
-
-  // weights: one buffer per matrix over this block's rows, so that rows past
-  // the block and quads past the last read as zero without touching memory
-  const int qrec = nrows * (K >> 1), srec = nrows * (K >> 4);
-  const __amdgpu_buffer_rsrc_t rq0 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.wq0) + (size_t)row_lo * (K >> 1), (short)0, qrec, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs0 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.ws0) + (size_t)row_lo * (K >> 4), (short)0, srec, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rq1 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.wq1) + (size_t)row_lo * (K >> 1), (short)0, qrec, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rs1 = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.ws1) + (size_t)row_lo * (K >> 4), (short)0, srec, kBufferWord3);
-  auto load_task = [&](uint4 (&q)[G][KJ], uint32_t (&sc)[G][KJ], int t) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int v = t * G + g;
-      const bool up = FUSED && (v & 1);
-      const int row = 4 * (FUSED ? (v >> 1) : v) + j;
-#pragma unroll
-      for (int kj = 0; kj < KJ; ++kj) {
-        const int c = beta + 16 * (KJ * wv + kj);
-        const u32x4_t v4 = __builtin_amdgcn_raw_buffer_load_b128(up ? rq1 : rq0, row * (K >> 1) + c * 16, 0,
-                                                                 kCpolNt);
-        q[g][kj] = make_uint4(v4.x, v4.y, v4.z, v4.w);
-        sc[g][kj] = __builtin_amdgcn_raw_buffer_load_b32(up ? rs1 : rs0, row * (K >> 4) + (c >> 1) * 4, 0,
-                                                         kCpolNt);
-      }
-    }
-  };
-  // partial of (quad v, weight row j, activation row m) from 16-lane row rho:
-  // red[(4 v + j) JS + m WR + 4 wv + rho]
+  // partial of (quad v, weight row j, activation row m) from wave wv's 16-lane
+  // row rho: red[(4 v + j) JS + m WR + 4 wv + rho]
   float* const park = red + j * JS + 4 * wv + (lane >> 4);
-  auto compute = [&](const uint4 (&q)[G][KJ], const uint32_t (&sc)[G][KJ], int t) {
+  float gv0 = 1.0f, gv1 = 1.0f;
+
+  // The wave's work for KJ = 1 or 2 columns (compile-time in each copy).
+  auto body = [&](auto kj_count) {
+    constexpr int KJ = decltype(kj_count)::value;
+    const int c0 = KJ == 2 ? 2 * wv : N2 + wv;  // this wave's first column
+    // x: lane (beta, j) holds activation rows 4 pp + j of chunk beta + 16 c
+    // for the wave's columns c = c0 + kj, as 16-byte units u = 0..3.  Loaded
+    // as one contiguous 1 KB row span per instruction (lane l: bytes 16 l..,
+    // i.e. unit l & 3 of chunk l >> 2 of row 4 pp + u in xv[..][u]) and then
+    // transposed within each quad of lanes through LDS (below).  Measured at
+    // M = 7 on the square (five waves of two columns): loading each lane's own
+    // units directly (16 bytes per lane at a 64-byte stride) 7.11 us per call,
+    // contiguous loads with a DPP transpose 6.70, with the LDS transpose 6.53.
+    // Rows >= M lie past the buffer's records and read as zero.
+    uint4 xv[KJ][P][4];
+    const int xlane = 16 * 64 * c0 + 16 * lane;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int v = t * G + g;
-      if (v < NQ) {
-        float acc[P][4];
+    for (int kj = 0; kj < KJ; ++kj)
 #pragma unroll
-        for (int pp = 0; pp < P; ++pp)
+      for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[pp][r] = 0.0f;
+        for (int u = 0; u < 4; ++u) {
+          const int off = xlane + ((4 * pp + u) * (K * 2) + 16 * 64 * kj);
+          const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+          xv[kj][pp][u] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+    // weights: one buffer per matrix over this block's rows, so that rows past
+    // the block and quads past the last read as zero without touching memory
+    const int qrec = nrows * (K >> 1), srec = nrows * (K >> 4);
+    const __amdgpu_buffer_rsrc_t rq0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.wq0) + (size_t)row_lo * (K >> 1), (short)0, qrec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs0 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.ws0) + (size_t)row_lo * (K >> 4), (short)0, srec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rq1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.wq1) + (size_t)row_lo * (K >> 1), (short)0, qrec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rs1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.ws1) + (size_t)row_lo * (K >> 4), (short)0, srec, kBufferWord3);
+    auto load_task = [&](uint4 (&q)[G][KJ], uint32_t (&sc)[G][KJ], int t) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int v = t * G + g;
+        const bool up = FUSED && (v & 1);
+        const int row = 4 * (FUSED ? (v >> 1) : v) + j;
 #pragma unroll
         for (int kj = 0; kj < KJ; ++kj) {
-          const uint4 qq = q[g][kj];
-          const uint32_t pr = sc[g][kj] >> shp;
-          const float s_lo = e4m3_to_f32<0>(pr), s_hi = e4m3_to_f32<1>(pr);
-          f32x4_t C[P];
-          // word wi holds inputs 8wi..8wi+7 of the chunk: two MFMAs of 4 inputs
-#define W4A16_XR_WORD(word, wi)                                                             \
-  {                                                                                        \
-    const i16x4_t b0 = pack4(fp4x2_to_bf16x2<0>(word), fp4x2_to_bf16x2<1>(word));          \
-    const i16x4_t b1 = pack4(fp4x2_to_bf16x2<2>(word), fp4x2_to_bf16x2<3>(word));          \
-    _Pragma("unroll") for (int pp = 0; pp < P; ++pp) {                                     \
-      C[pp] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(                                      \
-          pack4(xv[kj][pp][wi].x, xv[kj][pp][wi].y), b0, C[pp], 0, 0, 0);                  \
-      C[pp] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(                                      \
-          pack4(xv[kj][pp][wi].z, xv[kj][pp][wi].w), b1, C[pp], 0, 0, 0);                  \
-    }                                                                                      \
+          const int c = beta + 16 * (c0 + kj);
+          const u32x4_t v4 = __builtin_amdgcn_raw_buffer_load_b128(up ? rq1 : rq0, row * (K >> 1) + c * 16,
+                                                                   0, kCpolNt);
+          q[g][kj] = make_uint4(v4.x, v4.y, v4.z, v4.w);
+          sc[g][kj] = __builtin_amdgcn_raw_buffer_load_b32(up ? rs1 : rs0, row * (K >> 4) + (c >> 1) * 4, 0,
+                                                           kCpolNt);
+        }
+      }
+    };
+    auto compute = [&](const uint4 (&q)[G][KJ], const uint32_t (&sc)[G][KJ], int t) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int v = t * G + g;
+        if (v < NQ) {
+          float acc[P][4];
+#pragma unroll
+          for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[pp][r] = 0.0f;
+#pragma unroll
+          for (int kj = 0; kj < KJ; ++kj) {
+            const uint4 qq = q[g][kj];
+            const uint32_t pr = sc[g][kj] >> shp;
+            const float s_lo = e4m3_to_f32<0>(pr), s_hi = e4m3_to_f32<1>(pr);
+            f32x4_t C[P];
+            // word wi holds inputs 8wi..8wi+7 of the chunk: two MFMAs of 4 inputs
+#define W4A16_XR_WORD(word, wi)                                                           \
+  {                                                                                      \
+    const i16x4_t b0 = pack4(fp4x2_to_bf16x2<0>(word), fp4x2_to_bf16x2<1>(word));        \
+    const i16x4_t b1 = pack4(fp4x2_to_bf16x2<2>(word), fp4x2_to_bf16x2<3>(word));        \
+    _Pragma("unroll") for (int pp = 0; pp < P; ++pp) {                                   \
+      C[pp] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(                                    \
+          pack4(xv[kj][pp][wi].x, xv[kj][pp][wi].y), b0, C[pp], 0, 0, 0);                \
+      C[pp] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(                                    \
+          pack4(xv[kj][pp][wi].z, xv[kj][pp][wi].w), b1, C[pp], 0, 0, 0);                \
+    }                                                                                    \
   }
 #pragma unroll
-          for (int pp = 0; pp < P; ++pp) C[pp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          W4A16_XR_WORD(qq.x, 0)
-          W4A16_XR_WORD(qq.y, 1)
+            for (int pp = 0; pp < P; ++pp) C[pp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            W4A16_XR_WORD(qq.x, 0)
+            W4A16_XR_WORD(qq.y, 1)
 #pragma unroll
-          for (int pp = 0; pp < P; ++pp)
+            for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (4 * pp + r < M) acc[pp][r] = fmaf(C[pp][r], s_lo, acc[pp][r]);
+              for (int r = 0; r < 4; ++r)
+                if (4 * pp + r < M) acc[pp][r] = fmaf(C[pp][r], s_lo, acc[pp][r]);
 #pragma unroll
-          for (int pp = 0; pp < P; ++pp) C[pp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          W4A16_XR_WORD(qq.z, 2)
-          W4A16_XR_WORD(qq.w, 3)
+            for (int pp = 0; pp < P; ++pp) C[pp] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            W4A16_XR_WORD(qq.z, 2)
+            W4A16_XR_WORD(qq.w, 3)
 #pragma unroll
-          for (int pp = 0; pp < P; ++pp)
+            for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (4 * pp + r < M) acc[pp][r] = fmaf(C[pp][r], s_hi, acc[pp][r]);
+              for (int r = 0; r < 4; ++r)
+                if (4 * pp + r < M) acc[pp][r] = fmaf(C[pp][r], s_hi, acc[pp][r]);
 #undef W4A16_XR_WORD
+          }
+          // the 4 blocks of each 16-lane row (the same weight row j), summed by
+          // DPP with every lane active; lanes 16 rho + j then park the sums
+          float vv[P][4];
+#pragma unroll
+          for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (4 * pp + r < M) {
+                vv[pp][r] = dpp_add<kDppRor8>(dpp_add<kDppRor4>(acc[pp][r]));
+                // keep the DPP adds ahead of the writers' branch (inside it the
+                // masked-off lanes would be invalid DPP sources)
+                asm volatile("" : "+v"(vv[pp][r]));
+              }
+          if ((lane & 12) == 0) {
+            float* const dst = park + v * 4 * JS;
+#pragma unroll
+            for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (4 * pp + r < M) dst[(4 * pp + r) * WR] = vv[pp][r];
+          }
         }
-        // the 4 blocks of each 16-lane row (the same weight row j), summed by
-        // DPP with every lane active; lanes 16 rho + j then park the sums
-        float vv[P][4];
+      }
+    };
+
+    uint4 qa[G][KJ], qb[G][KJ];
+    uint32_t sa[G][KJ], sb[G][KJ];
+    load_task(qa, sa, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // g after the first loads: a scalar load's wait is lgkmcnt(0), which ahead
+    // of them would hold back every vector load's address set-up
+    typedef const __attribute__((address_space(4))) float cfloat;
+    gv0 = *reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(a.g0));
+    if (FUSED) gv1 = *reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(a.g1));
+    // x units into place, (lane 4 beta + k, unit u) <- (lane 4 beta + u, unit
+    // k), through this wave's LDS: unit u' for lane l is stored at [u'][l], so
+    // the reads are contiguous.  The area later holds partial sums of other
+    // waves, hence the barrier after every wave has read its own.
+    {
+      uint4* const xt = reinterpret_cast<uint4*>(red) + wv * (2 * P * 4 * 64);
+#pragma unroll
+      for (int kj = 0; kj < KJ; ++kj)
 #pragma unroll
         for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (4 * pp + r < M) {
-              vv[pp][r] = dpp_add<kDppRor8>(dpp_add<kDppRor4>(acc[pp][r]));
-              // keep the DPP adds ahead of the writers' branch (inside it the
-              // masked-off lanes would be invalid DPP sources)
-              asm volatile("" : "+v"(vv[pp][r]));
-            }
-        if ((lane & 12) == 0) {
-          float* const dst = park + v * 4 * JS;
+          for (int u = 0; u < 4; ++u) xt[((kj * P + pp) * 4 + j) * 64 + 4 * beta + u] = xv[kj][pp][u];
 #pragma unroll
-          for (int pp = 0; pp < P; ++pp)
+      for (int kj = 0; kj < KJ; ++kj)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (4 * pp + r < M) dst[(4 * pp + r) * WR] = vv[pp][r];
-        }
-      }
+        for (int pp = 0; pp < P; ++pp)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) xv[kj][pp][u] = xt[((kj * P + pp) * 4 + u) * 64 + lane];
+      lds_barrier();
+    }
+    // two tasks per iteration and one exit test (see the whole-row kernel)
+    int t = 0;
+    while (t < ntasks) {
+      load_task(qb, sb, t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(qa, sa, t);
+      load_task(qa, sa, t + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < ntasks) compute(qb, sb, t + 1);
+      t += 2;
     }
   };
+  if constexpr (N2 == W) {
+    body(std::integral_constant<int, 2>{});
+  } else {
+    if (wv < N2)
+      body(std::integral_constant<int, 2>{});
+    else
+      body(std::integral_constant<int, 1>{});
+  }
 
-  uint4 qa[G][KJ], qb[G][KJ];
-  uint32_t sa[G][KJ], sb[G][KJ];
-  load_task(qa, sa, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  // g after the first loads: a scalar load's wait is lgkmcnt(0), which ahead
-  // of them would hold back every vector load's address set-up
-  typedef const __attribute__((address_space(4))) float cfloat;
-  const float gv0 = *reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(a.g0));
-  const float gv1 = FUSED ? *reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(a.g1)) : 1.0f;
-  // x units into place, (lane 4 beta + k, unit u) <- (lane 4 beta + u, unit
-  // k), through this wave's 16 KB of LDS: unit u' for lane l is stored at
-  // [u'][l], so the reads are contiguous.  The region later holds partial
-  // sums of other waves, hence the barrier after every wave has read it.
-  {
-    uint4* const xt = reinterpret_cast<uint4*>(red) + wv * (KJ * P * 4 * 64);
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj)
-#pragma unroll
-      for (int pp = 0; pp < P; ++pp)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xt[((kj * P + pp) * 4 + j) * 64 + 4 * beta + u] = xv[kj][pp][u];
-#pragma unroll
-    for (int kj = 0; kj < KJ; ++kj)
-#pragma unroll
-      for (int pp = 0; pp < P; ++pp)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xv[kj][pp][u] = xt[((kj * P + pp) * 4 + u) * 64 + lane];
-    lds_barrier();
-  }
-  // two tasks per iteration and one exit test (see the whole-row kernel)
-  int t = 0;
-  while (t < ntasks) {
-    load_task(qb, sb, t + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(qa, sa, t);
-    load_task(qa, sa, t + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    if (t + 1 < ntasks) compute(qb, sb, t + 1);
-    t += 2;
-  }
   lds_barrier();
   const float ig0 = 1.0f / gv0, ig1 = 1.0f / gv1;
   for (int o = tid; o < nrows * M; o += 64 * W) {

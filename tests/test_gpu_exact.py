@@ -176,12 +176,30 @@ def test_k_column_kernel_fused_exact(M, N):
     fused_exact(M, N, 5120, 1900 + 11 * M + N, ctx="k-column fused")
 
 
+@pytest.mark.parametrize("M,N", [(5, 17408), (6, 16385), (7, 17408), (8, 17408), (8, 39936),
+                                 (8, 39937)])
+def test_k_column_kernel_eight_waves_exact(M, N):
+    """Row blocks of 16 or more quads at M >= 5 run 8 waves, two of which own
+    two chunk columns and six one; 39 936 rows at M = 8 (156 per block) are the
+    most whose 8-wave partials fit in LDS, 39 937 fall back to 5 waves.  16 385
+    leaves one row in the last quad of the first block."""
+    gemm_exact(M, N, 5120, 2000 + 11 * M + N % 89, "mant" if N % 2 else "pow2",
+               ctx=f"k-column 8 waves N={N}")
+
+
+@pytest.mark.parametrize("M", [6, 7])
+def test_k_column_kernel_eight_waves_fused_exact(M):
+    """Fused gate/up at 17 408 rows (34 quads per block): 8 waves."""
+    fused_exact(M, 17408, 5120, 2100 + M, ctx="k-column fused 8 waves")
+
+
 @pytest.mark.parametrize("M,N,fused", [(8, 63488, False), (8, 63489, False), (7, 35000, True),
                                          (7, 40000, True)])
 def test_k_column_kernel_lds_limit_exact(M, N, fused):
     """Either side of the largest N whose row blocks (one per CU) fit their
     partials in LDS: 63 488 rows plain at M = 8 (248 per block) still run the
-    K-column kernel, 63 489 the MFMA kernel; likewise fused at 35 000 / 40 000."""
+    K-column kernel (with 5 waves), 63 489 the MFMA kernel; likewise fused at
+    35 000 / 40 000."""
     if fused:
         fused_exact(M, N, 5120, 1960 + N % 97, ctx=f"k-column limit fused N={N}")
     else:
