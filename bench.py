@@ -370,6 +370,8 @@ def bench_configs(dev, stream, sq, extra=False):
             res["two_launches_graph"] = time_config([lambda s, i=i: call(s, i, False) for i in range(copies)],
                                                     stream, b)
             for one, name in ((True, "one_launch_eager"), (False, "two_launches_eager")):
+                if one and res["one_launch_possible"] != 1:
+                    continue  # the call would run as two launches
                 for i in range(copies):
                     call(stream, i, one)
                 torch.cuda.synchronize()

@@ -599,6 +599,10 @@ struct MlpPlan {
   size_t part1, part2, ws;  // byte offsets of the partials, total bytes
 };
 
+// The plan of one phase of the two-launch path: the whole-row and K-column
+// kernels where they apply, else the general kernels' plan.
+Plan mlp_launch_plan(int M, int N, int K, int epi) { return plan_gemm(M, N, K, epi, true, true); }
+
 MlpPlan plan_mlp(int M, int H, int F) {
   MlpPlan mp{};
   // the general kernels' plans: the persistent kernel runs their bodies, and
@@ -615,9 +619,13 @@ MlpPlan plan_mlp(int M, int H, int F) {
   // one launch: both phases on the same kernel family, block size and ring
   // depth, h addressable by 32-bit buffer offsets, and every workgroup of the
   // grid resident at once (the barrier waits for all of them)
+  // Not where the two-launch path takes the K-column kernel for either phase:
+  // its sums run in another order than the persistent kernel's bodies, and
+  // the two paths give the same bits.
   const Plan &a = mp.p1, &b = mp.p2;
   if (a.mfma != b.mfma || a.W != b.W || a.LB != b.LB || a.D != b.D ||
-      (size_t)M * F * 2 >= ((size_t)1 << 31))
+      (size_t)M * F * 2 >= ((size_t)1 << 31) || mlp_launch_plan(M, F, H, kEpiSwiglu).xr_cpl > 0 ||
+      mlp_launch_plan(M, H, F, kEpiPlain).xr_cpl > 0)
     return mp;
   const int rows = a.mfma ? (M + 3) / 4 : M;
   for (const MlpKernEntry& e : kMlpKernels)
@@ -697,10 +705,9 @@ w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace
     if (e == hipSuccess) return W4A16_OK;
     (void)hipGetLastError();  // clear the refused launch's error
   }
-  // two launches: each phase takes its own best plan among the kernels whose
-  // sums match the persistent kernel's bit for bit
-  const Plan q1 = plan_gemm(M, F, H, kEpiSwiglu, true, false),
-             q2 = plan_gemm(M, H, F, kEpiPlain, true, false);
+  // two launches: each phase takes its own best plan (the persistent kernel
+  // is planned only where that plan's sums match its own bit for bit)
+  const Plan q1 = mlp_launch_plan(M, F, H, kEpiSwiglu), q2 = mlp_launch_plan(M, H, F, kEpiPlain);
   if (q1.S == 0 || q2.S == 0 || q1.lds > kMaxLds || q2.lds > kMaxLds || q1.ws > mp.p1.ws ||
       q2.ws > mp.p2.ws)
     return W4A16_ERR_UNSUPPORTED;

@@ -205,8 +205,9 @@ w4a16_status_t w4a16_quantize_bf16(const uint16_t* w, uint8_t* wq, uint8_t* ws, 
  * By default the block runs as two kernels on `stream`.  With options->launch
  * = W4A16_MLP_ONE_LAUNCH both matmuls run in ONE persistent launch with a
  * device-wide barrier between them, when the two launch plans allow it (same
- * kernel family and block size, see w4a16_mlp_one_launch) and the stream is
- * not being captured into a graph.  That launch is cooperative: the runtime
+ * kernel family and block size, and neither phase on the K-column kernel
+ * that K = 5120 takes at 3 <= M <= 8; see w4a16_mlp_one_launch) and the
+ * stream is not being captured into a graph.  That launch is cooperative: the runtime
  * either makes every workgroup resident at once or refuses it, and a refused
  * launch falls back to the two kernels.  The results are bit-identical
  * either way.

@@ -123,17 +123,22 @@ def test_mlp_matches_oracle_both_paths(M, H, F):
     assert counters_zero(work1) and counters_zero(work2)
 
 
-@pytest.mark.parametrize("M", [1, 7])
-def test_mlp_full_size(M):
+@pytest.mark.parametrize("M,one", [(1, 1), (7, 0)])
+def test_mlp_full_size(M, one):
+    """At H = 5120 and 3 <= M <= 8 the gate/up phase takes the K-column kernel,
+    whose sums the persistent kernel does not reproduce: such shapes run as two
+    launches whatever the option (M = 7), others in one when asked (M = 1)."""
     H, F = 5120, 17408
-    assert w4.mlp_one_launch(M, H, F) == 1, "the benchmark shape should run in one launch"
+    assert w4.mlp_one_launch(M, H, F) == one
     say(f"[mlp full] M={M}")
     host, dev, x = block(300, M, H, F)
     y, work = run(dev, x, M, H, F, one_launch=True)
     check(y, host, x, M, H, F, f"full M={M}")
-    y2, _ = run(dev, x, M, H, F, one_launch=False)
+    y2, work2 = run(dev, x, M, H, F, one_launch=False)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
-    assert counters_zero(work)
+    ref_h = w4.gemm_gate_up_swiglu(*dev[0], *dev[1], d_bf16(x))
+    assert torch.equal(h_of(work2, M, F), ref_h.view(torch.int16)), "h differs from the gate/up entry point"
+    assert counters_zero(work) and counters_zero(work2)
 
 
 def test_barrier_timeout_is_flagged_and_recovers():
