@@ -214,81 +214,101 @@ bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
 }
 
 // K-column MFMA kernels with x in registers (k_gemm_xr), 3 <= M <= 8 at
-// K = 5120 (CPL = 5), plain and SwiGLU epilogues; other shapes take the MFMA
-// kernel.  (Measured on MI355X against the MFMA kernel, HIP-graph replay:
-// 5120 x 5120 at M = 3, 4, 5, 7, 8: 5.55 / 5.61 / 6.43 / 6.60 / 6.68 us
-// against 7.02 / 7.07 / 7.85 / 7.99 / 8.01; gate/up 2 x 17408 x 5120 at
-// M = 4, 5, 7, 8: 20.2 / 21.2 / 21.6 / 21.8 us against 22.1 / 23.3 / 23.9 /
-// 24.3.)
+// K = 5120 (CPL = 5; plain and SwiGLU epilogues), and 5 <= M <= 8 at K =
+// 17408 (CPL = 17, the down projection; plain, in two K-slices of 17
+// columns); other shapes take the MFMA kernel.  (Measured on MI355X against the MFMA kernel,
+// HIP-graph replay: 5120 x 5120 at M = 3, 4, 5, 7, 8: 5.55 / 5.61 / 6.43 /
+// 6.60 / 6.68 us against 7.02 / 7.07 / 7.85 / 7.99 / 8.01; gate/up 2 x 17408
+// x 5120 at M = 4, 5, 7, 8: 20.2 / 21.2 / 21.6 / 21.8 us against 22.1 / 23.3
+// / 23.9 / 24.3.)
 struct XrEntry {
-  int M, cpl, epi, W;
+  int M, cpl, epi, W, S;
   const void* fn;
 };
-#define W4A16_XE(MM, F, WW) {MM, 5, F, WW, reinterpret_cast<const void*>(&k_gemm_xr<MM, 5, F, WW>)},
-#define W4A16_XE_P2(F, WW) W4A16_XE(5, F, WW) W4A16_XE(6, F, WW) W4A16_XE(7, F, WW) W4A16_XE(8, F, WW)
-#define W4A16_XE_ALL(F, WW) W4A16_XE(3, F, WW) W4A16_XE(4, F, WW) W4A16_XE_P2(F, WW)
-const XrEntry kXrKernels[] = {W4A16_XE_ALL(kEpiPlain, 5) W4A16_XE_ALL(kEpiSwiglu, 5)
-                              W4A16_XE_P2(kEpiPlain, 8) W4A16_XE_P2(kEpiSwiglu, 8)};
+#define W4A16_XE(MM, C, F, WW, SS) \
+  {MM, C, F, WW, SS, reinterpret_cast<const void*>(&k_gemm_xr<MM, C, F, WW, SS>)},
+#define W4A16_XE_P2(C, F, WW, SS) \
+  W4A16_XE(5, C, F, WW, SS) W4A16_XE(6, C, F, WW, SS) W4A16_XE(7, C, F, WW, SS) W4A16_XE(8, C, F, WW, SS)
+#define W4A16_XE_ALL(C, F, WW, SS) W4A16_XE(3, C, F, WW, SS) W4A16_XE(4, C, F, WW, SS) W4A16_XE_P2(C, F, WW, SS)
+const XrEntry kXrKernels[] = {W4A16_XE_ALL(5, kEpiPlain, 5, 1) W4A16_XE_ALL(5, kEpiSwiglu, 5, 1)
+                              W4A16_XE_P2(5, kEpiPlain, 8, 1) W4A16_XE_P2(5, kEpiSwiglu, 8, 1)
+                              W4A16_XE_P2(17, kEpiPlain, 9, 2)};
 #undef W4A16_XE_ALL
 #undef W4A16_XE_P2
 #undef W4A16_XE
-const void* find_xr_kernel(int M, int cpl, int epi, int W) {
+const void* find_xr_kernel(int M, int cpl, int epi, int W, int S) {
   for (const XrEntry& e : kXrKernels)
-    if (e.M == M && e.cpl == cpl && e.epi == epi && e.W == W) return e.fn;
+    if (e.M == M && e.cpl == cpl && e.epi == epi && e.W == W && e.S == S) return e.fn;
   return nullptr;
 }
-// LDS bytes of k_gemm_xr<M, ..., W> for a row block of `rows` rows: one fp32
-// partial per (quad, weight row, activation row, wave, 16-lane row), the
-// floats per (quad, weight row) padded to 4 mod 8, as in the kernel; at least
-// the area the waves first stage their x in (up to 2 columns x P passes x 4
-// units x 64 lanes x 16 bytes per wave)
-size_t xr_lds(int M, bool fused, long long rows, int W) {
+// LDS bytes of k_gemm_xr<M, ..., W, S> for a row block of `rows` rows and a
+// K-slice of jt columns: one fp32 partial per (quad, weight row, activation
+// row, wave, 16-lane row), the floats per (quad, weight row) padded to 4 mod
+// 8, as in the kernel; at least the area the waves first stage their x in
+// (per column: P passes x 4 units x 64 lanes x 16 bytes)
+size_t xr_lds(int M, bool fused, long long rows, int W, int jt) {
   const size_t quads = (size_t)((rows + 3) / 4) * (fused ? 2 : 1);
   size_t js = (size_t)M * 4 * (size_t)W;
   js += js % 8 == 0 ? 4 : 0;
   const size_t partials = quads * 4 * js * sizeof(float);
-  const size_t x_stage = (size_t)W * 2 * ((M + 3) / 4) * 4 * 64 * 16;
+  const size_t x_stage = (size_t)jt * ((M + 3) / 4) * 4 * 64 * 16;
   return partials > x_stage ? partials : x_stage;
 }
 
-// Plan for the K-column kernel, or false if it does not apply: one row block
-// per CU, whose partials must fit in LDS (N up to ~63 000 plain, ~31 000
-// fused at M = 8, with 5 waves).  More blocks would each load x again: on the 5120 ->
-// 248 320 head at M = 7, 1024 blocks took 154.6 us against 145.6 for the MFMA
-// kernel (measured on MI355X), so larger N takes the MFMA kernel.  Waves:
-// 2 CPL / 2 (two columns each), except 8 for M >= 5 once a block has 16 or
-// more row quads (the first two columns to some waves, one to the rest; two
-// waves per SIMD; 5 again where 8 waves' partials would not fit): measured
-// at M = 7, the square (5 quads per block) 6.55 us with 5 waves, 6.69 with 8;
-// gate/up (34 quads) 22.5 with 5, 21.6 with 8; at M = 3 gate/up 20.1 with 5,
-// 20.3 with 8.
+// Plan for the K-column kernel, or false if it does not apply: one workgroup
+// per CU, whose partials must fit in LDS (K = 5120: N up to ~63 000 plain,
+// ~31 000 fused at M = 8, with 5 waves).  More workgroups would each load x
+// again: on the 5120 -> 248 320 head at M = 7, 1024 blocks took 154.6 us
+// against 145.6 for the MFMA kernel (measured on MI355X), so larger N takes
+// the MFMA kernel.  K = 5120, waves: 2 CPL / 2 (two columns each), except 8
+// for M >= 5 once a block has 16 or more row quads (the first two columns to
+// some waves, one to the rest; two waves per SIMD; 5 again where 8 waves'
+// partials would not fit): measured at M = 7, the square (5 quads per block)
+// 6.55 us with 5 waves, 6.69 with 8; gate/up (34 quads) 22.5 with 5, 21.6
+// with 8; at M = 3 gate/up 20.1 with 5, 20.3 with 8.  K = 17408: 34 columns
+// of x do not fit one workgroup's registers at two or three per wave, so
+// the row blocks are half as many and each has two workgroups, one per
+// K-slice of 17 columns (split-K partials in the workspace), of 9 waves: 8
+// of two columns and one of one.  (16 waves, one of two columns and 15 of
+// one, would leave 128 VGPRs per wave: the two-column wave spills.)
+// Measured, 5120 x 17408 at M = 5 / 6 / 7 / 8: 15.1 / 15.5 / 15.5 / 15.9 us
+// against 16.5 / 16.9 / 17.0 / 17.3 for the MFMA kernel (also two K-slices);
+// at M = 3 / 4 (one pass of activation rows) 14.6 / 14.7 against 13.9 / 14.3,
+// so those stay on the MFMA kernel.
 bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
   if (M < 3 || M > 8 || epi == kEpiArgmax || K % 1024 != 0) return false;
 #ifdef W4A16_TUNING
   if (g_override.enable) return false;
 #endif
   const int cpl = K / 1024;
+  const int S = cpl == 17 ? 2 : 1;
+  const int jt = 2 * cpl / S;
   const bool fused = epi == kEpiSwiglu;
-  long long nrb = cu_count();
+  long long nrb = cu_count() / S;
   if (nrb > N) nrb = N;
   if (nrb < 1) nrb = 1;
   const long long rows = N / nrb + (N % nrb > 0);
   const long long quads = (rows + 3) / 4 * (fused ? 2 : 1);
-  int W = quads >= 16 && M >= 5 ? 8 : cpl;
-  if (W != cpl && xr_lds(M, fused, rows, W) > kMaxLds) W = cpl;  // fewer partials per quad
-  if (!find_xr_kernel(M, cpl, epi, W)) return false;
-  if (xr_lds(M, fused, rows, W) > kMaxLds) return false;
+  int W;
+  if (S > 1) {
+    W = 9;
+  } else {
+    W = quads >= 16 && M >= 5 ? 8 : cpl;
+    if (W != cpl && xr_lds(M, fused, rows, W, jt) > kMaxLds) W = cpl;  // fewer partials per quad
+  }
+  if (!find_xr_kernel(M, cpl, epi, W, S)) return false;
+  if (xr_lds(M, fused, rows, W, jt) > kMaxLds) return false;
   pl = Plan{};
   pl.mfma = true;
   pl.lr = 1;
   pl.W = W;
   pl.LB = 64 * W;
   pl.nrb = (int)nrb;
-  pl.S = 1;
+  pl.S = S;
   pl.rq = N / (int)nrb;
   pl.rr = N % (int)nrb;
-  pl.lds = xr_lds(M, fused, pl.rq + (pl.rr > 0), W);
-  pl.ws = 0;
+  pl.lds = xr_lds(M, fused, pl.rq + (pl.rr > 0), W, jt);
+  pl.ws = S > 1 ? kCounterBytes + (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1) : 0;
   pl.xr_cpl = cpl;
   return true;
 }
@@ -459,9 +479,11 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t
 
 hipError_t dispatch(const Plan& pl, int epi, hipStream_t s, const MatArgs& a) {
   if (pl.xr_cpl > 0) {
-    const void* fn = find_xr_kernel(a.M, pl.xr_cpl, epi, pl.W);
-    if (!fn || pl.W * 64 != pl.LB || a.K != 1024 * pl.xr_cpl) return hipErrorInvalidConfiguration;
-    return launch(fn, dim3((unsigned)pl.nrb), dim3((unsigned)(pl.W * 64)), pl.lds, s, a);
+    const void* fn = find_xr_kernel(a.M, pl.xr_cpl, epi, pl.W, pl.S);
+    if (!fn || pl.W * 64 != pl.LB || a.K != 1024 * pl.xr_cpl || a.S != pl.S ||
+        (pl.S > 1 && (a.part == nullptr || a.cnt == nullptr)))
+      return hipErrorInvalidConfiguration;
+    return launch(fn, dim3((unsigned)pl.nrb, (unsigned)pl.S), dim3((unsigned)(pl.W * 64)), pl.lds, s, a);
   }
   if (pl.rows_cpl > 0) {
     const void* fn = find_rows_kernel(a.M, pl.rows_cpl, epi);
@@ -593,6 +615,8 @@ constexpr int kMlpSpinDefault = 1 << 20;
 
 struct MlpPlan {
   Plan p1, p2;              // gate/up (N = F, K = H) and down (N = H, K = F)
+  Plan l1, l2;              // the same phases' plans for two launches
+  size_t cap1, cap2;        // workspace bytes each phase may use (counters included)
   const MlpKernEntry* k;    // persistent kernel, or nullptr: two launches
   int grid;
   size_t lds;
@@ -609,10 +633,14 @@ MlpPlan plan_mlp(int M, int H, int F) {
   // their workspace covers every variant (the whole-row kernel needs none)
   mp.p1 = plan_gemm(M, F, H, kEpiSwiglu, false, false);
   mp.p2 = plan_gemm(M, H, F, kEpiPlain, false, false);
-  if (mp.p1.S == 0 || mp.p2.S == 0) return MlpPlan{};
+  mp.l1 = mlp_launch_plan(M, F, H, kEpiSwiglu);
+  mp.l2 = mlp_launch_plan(M, H, F, kEpiPlain);
+  if (mp.p1.S == 0 || mp.p2.S == 0 || mp.l1.S == 0 || mp.l2.S == 0) return MlpPlan{};
+  mp.cap1 = mp.p1.ws > mp.l1.ws ? mp.p1.ws : mp.l1.ws;
+  mp.cap2 = mp.p2.ws > mp.l2.ws ? mp.p2.ws : mp.l2.ws;
   const size_t h_bytes = align256((size_t)M * F * 2);
-  const size_t w1 = mp.p1.ws > 0 ? align256(mp.p1.ws - kCounterBytes) : 0;
-  const size_t w2 = mp.p2.ws > 0 ? align256(mp.p2.ws - kCounterBytes) : 0;
+  const size_t w1 = mp.cap1 > 0 ? align256(mp.cap1 - kCounterBytes) : 0;
+  const size_t w2 = mp.cap2 > 0 ? align256(mp.cap2 - kCounterBytes) : 0;
   mp.part1 = kMlpHOffset + h_bytes;
   mp.part2 = mp.part1 + w1;
   mp.ws = mp.part2 + w2;
@@ -624,8 +652,7 @@ MlpPlan plan_mlp(int M, int H, int F) {
   // the two paths give the same bits.
   const Plan &a = mp.p1, &b = mp.p2;
   if (a.mfma != b.mfma || a.W != b.W || a.LB != b.LB || a.D != b.D ||
-      (size_t)M * F * 2 >= ((size_t)1 << 31) || mlp_launch_plan(M, F, H, kEpiSwiglu).xr_cpl > 0 ||
-      mlp_launch_plan(M, H, F, kEpiPlain).xr_cpl > 0)
+      (size_t)M * F * 2 >= ((size_t)1 << 31) || mp.l1.xr_cpl > 0 || mp.l2.xr_cpl > 0)
     return mp;
   const int rows = a.mfma ? (M + 3) / 4 : M;
   for (const MlpKernEntry& e : kMlpKernels)
@@ -707,9 +734,8 @@ w4a16_status_t run_mlp(const MatArgs& up0, const MatArgs& down0, void* workspace
   }
   // two launches: each phase takes its own best plan (the persistent kernel
   // is planned only where that plan's sums match its own bit for bit)
-  const Plan q1 = mlp_launch_plan(M, F, H, kEpiSwiglu), q2 = mlp_launch_plan(M, H, F, kEpiPlain);
-  if (q1.S == 0 || q2.S == 0 || q1.lds > kMaxLds || q2.lds > kMaxLds || q1.ws > mp.p1.ws ||
-      q2.ws > mp.p2.ws)
+  const Plan &q1 = mp.l1, &q2 = mp.l2;
+  if (q1.lds > kMaxLds || q2.lds > kMaxLds || q1.ws > mp.cap1 || q2.ws > mp.cap2)
     return W4A16_ERR_UNSUPPORTED;
   prepare(up, q1, reinterpret_cast<int*>(w), reinterpret_cast<float*>(w + mp.part1));
   prepare(down, q2, reinterpret_cast<int*>(w + kCounterBytes),

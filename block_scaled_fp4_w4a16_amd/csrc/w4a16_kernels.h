@@ -204,7 +204,8 @@ __device__ unsigned long long* w4a16_trace;
     const int ln = threadIdx.x & 63;                                                        \
     unsigned long long mine = 0;                                                            \
     for (int i = 0; i < 6; ++i) mine = ln == i ? tv[i] : mine;                              \
-    if (ln < 6) w4a16_trace[((size_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 8 + ln] = mine; \
+    const size_t wg = (size_t)blockIdx.y * gridDim.x + blockIdx.x;                         \
+    if (ln < 6) w4a16_trace[(wg * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 8 + ln] = mine;  \
   }
 #else
 #define W4A16_STAMP(var) const unsigned long long var = 0
@@ -1050,7 +1051,8 @@ __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows
 
 // ---------------------------------------------------------------------------
 // K-column MFMA kernel with x in registers, 3 <= M <= 8, K = 1024 * CPL
-// (CPL = 5: the hidden size of the square projections and of gate/up).
+// (CPL = 5: the hidden size of the square projections and of gate/up; CPL =
+// 17: the down projection's input, in S = 2 K-slices).
 //
 // The 4x4x4 block product of the MFMA kernel below (block beta = one chunk
 // column, its 4 columns = 4 weight rows, its 4 rows = activation rows; P
@@ -1067,19 +1069,23 @@ __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows
 // after the loop each output adds its 4 W partials in a fixed order.  Fused:
 // quad 2i holds gate rows 4i..4i+3, quad 2i+1 the same up rows.  A task is
 // two quads; two tasks are in registers, the next one's loads issued before
-// the current one is computed (the whole-row kernel's loop).
+// the current one is computed (the whole-row kernel's loop).  With S > 1 K-
+// slices, workgroup (rb, ks) covers columns ks JT .. ks JT + JT - 1 of row
+// block rb and parks its sums in the split-K partials; the row block's last
+// workgroup adds the slices in order (splitk_finish).
 // Measured on MI355X (HIP-graph replay, 64 / 32 cycled copies): 5120 x 5120
 // at M = 7 in 6.55 us with 5 waves (6.69 with 8) against 7.99 for the MFMA
 // kernel; gate/up 2 x 17408 x 5120 at M = 7 in 21.6 us with 8 waves (22.5
 // with 5) against 23.9.
 // ---------------------------------------------------------------------------
-template <int M, int CPL, int EPI, int W>
+template <int M, int CPL, int EPI, int W, int S>
 __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   constexpr bool FUSED = EPI == kEpiSwiglu;
   constexpr int P = (M + 3) / 4;
   constexpr int K = 1024 * CPL;
-  constexpr int JT = 2 * CPL;    // chunk columns of 16 chunks
-  constexpr int N2 = JT - W;     // waves 0..N2-1 own two columns, the rest one
+  static_assert((2 * CPL) % S == 0, "K-slices of whole columns");
+  constexpr int JT = 2 * CPL / S;  // chunk columns of 16 chunks in this K-slice
+  constexpr int N2 = JT - W;       // waves 0..N2-1 own two columns, the rest one
   static_assert(W <= JT && JT <= 2 * W, "every wave owns one or two columns");
   constexpr int G = 2;           // quads per task
   constexpr int WR = 4 * W;      // partials per (quad, weight row, activation row)
@@ -1087,10 +1093,14 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   // rows x 4 lane rows) of a partial then hit 16 distinct banks
   constexpr int JS = M * WR + ((M * WR) % 8 == 0 ? 4 : 0);
   static_assert(M >= 3 && M <= 8, "the K-column kernel serves 3 <= M <= 8");
-  extern __shared__ float red[];
+  // 16-byte aligned (x units and partials are read as uint4 / float4), also
+  // behind the static LDS of the split-K finish
+  extern __shared__ uint4 red_lds[];
+  float* const red = reinterpret_cast<float*>(red_lds);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rb = blockIdx.x;
+  const int ks = S > 1 ? (int)blockIdx.y : 0;  // K-slice: columns ks JT .. ks JT + JT - 1
   const int row_lo = rb * a.rq + (rb < a.rr ? rb : a.rr);
   const int row_hi = row_lo + a.rq + (rb < a.rr ? 1 : 0);
   const int nrows = row_hi - row_lo;
@@ -1106,11 +1116,16 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   // row rho: red[(4 v + j) JS + m WR + 4 wv + rho]
   float* const park = red + j * JS + 4 * wv + (lane >> 4);
   float gv0 = 1.0f, gv1 = 1.0f;
+  W4A16_STAMP(t_start);
+#ifdef W4A16_TRACE
+  unsigned long long t_issued = 0, t_barrier = 0, t_first = 0, t_end = 0;
+#endif
 
   // The wave's work for KJ = 1 or 2 columns (compile-time in each copy).
   auto body = [&](auto kj_count) {
     constexpr int KJ = decltype(kj_count)::value;
-    const int c0 = KJ == 2 ? 2 * wv : N2 + wv;  // this wave's first column
+    const int c0 = KJ == 2 ? 2 * wv : N2 + wv;  // this wave's first column in the slice
+    const int cg = ks * JT + c0;                 // ... in the row
     // x: lane (beta, j) holds activation rows 4 pp + j of chunk beta + 16 c
     // for the wave's columns c = c0 + kj, as 16-byte units u = 0..3.  Loaded
     // as one contiguous 1 KB row span per instruction (lane l: bytes 16 l..,
@@ -1121,7 +1136,7 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
     // contiguous loads with a DPP transpose 6.70, with the LDS transpose 6.53.
     // Rows >= M lie past the buffer's records and read as zero.
     uint4 xv[KJ][P][4];
-    const int xlane = 16 * 64 * c0 + 16 * lane;
+    const int xlane = 16 * 64 * cg + 16 * lane;
 #pragma unroll
     for (int kj = 0; kj < KJ; ++kj)
 #pragma unroll
@@ -1151,7 +1166,7 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
         const int row = 4 * (FUSED ? (v >> 1) : v) + j;
 #pragma unroll
         for (int kj = 0; kj < KJ; ++kj) {
-          const int c = beta + 16 * (c0 + kj);
+          const int c = beta + 16 * (cg + kj);
           const u32x4_t v4 = __builtin_amdgcn_raw_buffer_load_b128(up ? rq1 : rq0, row * (K >> 1) + c * 16,
                                                                    0, kCpolNt);
           q[g][kj] = make_uint4(v4.x, v4.y, v4.z, v4.w);
@@ -1237,42 +1252,60 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
     uint32_t sa[G][KJ], sb[G][KJ];
     load_task(qa, sa, 0);
     __builtin_amdgcn_sched_barrier(0);
+#ifdef W4A16_TRACE
+#ifdef W4A16_TRACE_XWAIT
+    __builtin_amdgcn_s_waitcnt(0);
+#endif
+    t_issued = wall_clock64();
+#endif
     // g after the first loads: a scalar load's wait is lgkmcnt(0), which ahead
     // of them would hold back every vector load's address set-up
     typedef const __attribute__((address_space(4))) float cfloat;
     gv0 = *reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(a.g0));
     if (FUSED) gv1 = *reinterpret_cast<cfloat*>(reinterpret_cast<uintptr_t>(a.g1));
     // x units into place, (lane 4 beta + k, unit u) <- (lane 4 beta + u, unit
-    // k), through this wave's LDS: unit u' for lane l is stored at [u'][l], so
-    // the reads are contiguous.  The area later holds partial sums of other
-    // waves, hence the barrier after every wave has read its own.
+    // k), through the LDS area of this wave's columns (P x 4 x 64 units per
+    // column): unit u' for lane l is stored at [u'][l ^ u'] (a swap within
+    // each quad of lanes, so that the 16 lanes of a row write 16 distinct
+    // bank groups; the reads stay 16-byte units of one 1 KB span).  The area
+    // later holds partial sums of other waves, hence the barrier after every
+    // wave has read its own.
     {
-      uint4* const xt = reinterpret_cast<uint4*>(red) + wv * (2 * P * 4 * 64);
+      uint4* const xt = reinterpret_cast<uint4*>(red) + c0 * (P * 4 * 64);
 #pragma unroll
       for (int kj = 0; kj < KJ; ++kj)
 #pragma unroll
         for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) xt[((kj * P + pp) * 4 + j) * 64 + 4 * beta + u] = xv[kj][pp][u];
+          for (int u = 0; u < 4; ++u) xt[((kj * P + pp) * 4 + j) * 64 + 4 * beta + (u ^ j)] = xv[kj][pp][u];
 #pragma unroll
       for (int kj = 0; kj < KJ; ++kj)
 #pragma unroll
         for (int pp = 0; pp < P; ++pp)
 #pragma unroll
-          for (int u = 0; u < 4; ++u) xv[kj][pp][u] = xt[((kj * P + pp) * 4 + u) * 64 + lane];
+          for (int u = 0; u < 4; ++u) xv[kj][pp][u] = xt[((kj * P + pp) * 4 + u) * 64 + (lane ^ u)];
       lds_barrier();
     }
+#ifdef W4A16_TRACE
+    t_barrier = wall_clock64();
+#endif
     // two tasks per iteration and one exit test (see the whole-row kernel)
     int t = 0;
     while (t < ntasks) {
       load_task(qb, sb, t + 1);
       __builtin_amdgcn_sched_barrier(0);
       compute(qa, sa, t);
+#ifdef W4A16_TRACE
+      if (t_first == 0) t_first = wall_clock64();
+#endif
       load_task(qa, sa, t + 2);
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 < ntasks) compute(qb, sb, t + 1);
       t += 2;
     }
+#ifdef W4A16_TRACE
+    t_end = wall_clock64();
+#endif
   };
   if constexpr (N2 == W) {
     body(std::integral_constant<int, 2>{});
@@ -1289,27 +1322,36 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
     const int n = o / M, m = o - n * M;
     const int vg = FUSED ? 2 * (n >> 2) : (n >> 2);
     const float4* pg = reinterpret_cast<const float4*>(red + (4 * vg + (n & 3)) * JS + m * WR);
-    float sg = 0.0f;
+    float sg = 0.0f, su = 0.0f;
 #pragma unroll
     for (int w = 0; w < W; ++w) {
       const float4 f = pg[w];
       sg += (f.x + f.y) + (f.z + f.w);
     }
-    uint16_t out;
     if (FUSED) {
       const float4* pu = reinterpret_cast<const float4*>(red + (4 * vg + 4 + (n & 3)) * JS + m * WR);
-      float su = 0.0f;
 #pragma unroll
       for (int w = 0; w < W; ++w) {
         const float4 f = pu[w];
         su += (f.x + f.y) + (f.z + f.w);
       }
-      out = f32_to_bf16(silu(sg * ig0) * (su * ig1));
-    } else {
-      out = f32_to_bf16(sg * ig0);
     }
-    a.y[(size_t)m * a.N + row_lo + n] = out;
+    const size_t i = (size_t)m * a.N + row_lo + n;
+    if (S > 1) {
+      // this K-slice's sums; the row block's last workgroup adds the slices
+      store_coherent(a.part + (size_t)ks * M * a.N + i, sg);
+      if (FUSED) store_coherent(a.part + (size_t)(S + ks) * M * a.N + i, su);
+    } else if (FUSED) {
+      a.y[i] = f32_to_bf16(silu(sg * ig0) * (su * ig1));
+    } else {
+      a.y[i] = f32_to_bf16(sg * ig0);
+    }
   }
+  if (S > 1) splitk_finish<FUSED, false>(a, rb, row_lo, nrows, ig0, ig1);
+#ifdef W4A16_TRACE
+  W4A16_STAMP(t_done);
+  W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);
+#endif
 }
 
 // ---------------------------------------------------------------------------

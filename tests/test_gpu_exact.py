@@ -193,6 +193,24 @@ def test_k_column_kernel_eight_waves_fused_exact(M):
     fused_exact(M, 17408, 5120, 2100 + M, ctx="k-column fused 8 waves")
 
 
+@pytest.mark.parametrize("M", [3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N", [1, 3, 129, 5121])
+def test_k_column_kernel_two_slices_exact(M, N):
+    """K = 17 408 at M >= 5: two workgroups per row block, one per K-slice of
+    17 columns, added by the row block's last workgroup (M = 3, 4: the MFMA
+    kernel); fewer rows than row blocks, a ragged row block and a ragged last
+    quad."""
+    gemm_exact(M, N, 17408, 2200 + 11 * M + N % 97, "mant" if (M + N) % 2 else "pow2",
+               ctx="k-column two slices")
+
+
+@pytest.mark.parametrize("N", [17920, 17921])
+def test_k_column_kernel_two_slices_lds_limit_exact(N):
+    """17 920 rows at M = 8 (140 per row block) are the most whose partials
+    fit in LDS; 17 921 take the MFMA kernel."""
+    gemm_exact(8, N, 17408, 2300 + N % 97, "pow2", ctx=f"k-column two slices limit N={N}")
+
+
 @pytest.mark.parametrize("M,N,fused", [(8, 63488, False), (8, 63489, False), (7, 35000, True),
                                          (7, 40000, True)])
 def test_k_column_kernel_lds_limit_exact(M, N, fused):
