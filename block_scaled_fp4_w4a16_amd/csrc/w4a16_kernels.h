@@ -1134,7 +1134,7 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
     // M = 7 on the square (five waves of two columns): loading each lane's own
     // units directly (16 bytes per lane at a 64-byte stride) 7.11 us per call,
     // contiguous loads with a DPP transpose 6.70, with the LDS transpose 6.53.
-    // Rows >= M lie past the buffer's records and read as zero.
+    // Rows M..4P-1 are zero without a load.
     uint4 xv[KJ][P][4];
     const int xlane = 16 * 64 * cg + 16 * lane;
 #pragma unroll
@@ -1143,6 +1143,10 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
       for (int pp = 0; pp < P; ++pp)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
+          if (4 * pp + u >= M) {  // a padding row: no load
+            xv[kj][pp][u] = make_uint4(0u, 0u, 0u, 0u);
+            continue;
+          }
           const int off = xlane + ((4 * pp + u) * (K * 2) + 16 * 64 * kj);
           const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
           xv[kj][pp][u] = make_uint4(v.x, v.y, v.z, v.w);
