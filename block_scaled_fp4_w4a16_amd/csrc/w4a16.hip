@@ -243,12 +243,13 @@ const void* find_xr_kernel(int M, int cpl, int epi, int W, int S) {
 }
 // LDS bytes of k_gemm_xr<M, ..., W, S> for a row block of `rows` rows and a
 // K-slice of jt columns: one fp32 partial per (quad, weight row, activation
-// row, wave, 16-lane row), the floats per (quad, weight row) padded to 4 mod
-// 8, as in the kernel; at least the area the waves first stage their x in
+// row, wave, 16-lane row; per activation row padded to an odd number of
+// 16-byte units), the floats per (quad, weight row) padded to 4 mod 8, as in
+// the kernel; at least the area the waves first stage their x in
 // (per column: P passes x 4 units x 64 lanes x 16 bytes)
 size_t xr_lds(int M, bool fused, long long rows, int W, int jt) {
   const size_t quads = (size_t)((rows + 3) / 4) * (fused ? 2 : 1);
-  size_t js = (size_t)M * 4 * (size_t)W;
+  size_t js = (size_t)M * (4 * (size_t)W + (W % 2 == 0 ? 4 : 0));
   js += js % 8 == 0 ? 4 : 0;
   const size_t partials = quads * 4 * js * sizeof(float);
   const size_t x_stage = (size_t)jt * ((M + 3) / 4) * 4 * 64 * 16;

@@ -1088,7 +1088,10 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   constexpr int N2 = JT - W;       // waves 0..N2-1 own two columns, the rest one
   static_assert(W <= JT && JT <= 2 * W, "every wave owns one or two columns");
   constexpr int G = 2;           // quads per task
-  constexpr int WR = 4 * W;      // partials per (quad, weight row, activation row)
+  // floats per (quad, weight row, activation row): 4 W partials, padded to an
+  // odd number of 16-byte units, so that the combine's float4 reads of
+  // consecutive activation rows (consecutive threads) spread over the banks
+  constexpr int WR = 4 * W + (W % 2 == 0 ? 4 : 0);
   // LDS floats per (quad, weight row), = 4 mod 8: the 16 writer lanes (4 weight
   // rows x 4 lane rows) of a partial then hit 16 distinct banks
   constexpr int JS = M * WR + ((M * WR) % 8 == 0 ? 4 : 0);

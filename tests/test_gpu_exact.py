@@ -176,12 +176,12 @@ def test_k_column_kernel_fused_exact(M, N):
     fused_exact(M, N, 5120, 1900 + 11 * M + N, ctx="k-column fused")
 
 
-@pytest.mark.parametrize("M,N", [(5, 17408), (6, 16385), (7, 17408), (8, 17408), (8, 39936),
-                                 (8, 39937)])
+@pytest.mark.parametrize("M,N", [(5, 17408), (6, 16385), (7, 17408), (8, 17408), (8, 35840),
+                                 (8, 35841)])
 def test_k_column_kernel_eight_waves_exact(M, N):
     """Row blocks of 16 or more quads at M >= 5 run 8 waves, two of which own
-    two chunk columns and six one; 39 936 rows at M = 8 (156 per block) are the
-    most whose 8-wave partials fit in LDS, 39 937 fall back to 5 waves.  16 385
+    two chunk columns and six one; 35 840 rows at M = 8 (140 per block) are the
+    most whose 8-wave partials fit in LDS, 35 841 fall back to 5 waves.  16 385
     leaves one row in the last quad of the first block."""
     gemm_exact(M, N, 5120, 2000 + 11 * M + N % 89, "mant" if N % 2 else "pow2",
                ctx=f"k-column 8 waves N={N}")
