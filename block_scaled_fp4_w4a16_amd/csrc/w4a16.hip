@@ -231,6 +231,7 @@ struct XrEntry {
   W4A16_XE(5, C, F, WW, SS) W4A16_XE(6, C, F, WW, SS) W4A16_XE(7, C, F, WW, SS) W4A16_XE(8, C, F, WW, SS)
 #define W4A16_XE_ALL(C, F, WW, SS) W4A16_XE(3, C, F, WW, SS) W4A16_XE(4, C, F, WW, SS) W4A16_XE_P2(C, F, WW, SS)
 const XrEntry kXrKernels[] = {W4A16_XE_ALL(5, kEpiPlain, 5, 1) W4A16_XE_ALL(5, kEpiSwiglu, 5, 1)
+                              W4A16_XE_P2(5, kEpiPlain, 6, 1) W4A16_XE_P2(5, kEpiSwiglu, 6, 1)
                               W4A16_XE_P2(5, kEpiPlain, 8, 1) W4A16_XE_P2(5, kEpiSwiglu, 8, 1)
                               W4A16_XE_P2(17, kEpiPlain, 9, 2)};
 #undef W4A16_XE_ALL
@@ -261,12 +262,17 @@ size_t xr_lds(int M, bool fused, long long rows, int W, int jt) {
 // ~31 000 fused at M = 8, with 5 waves).  More workgroups would each load x
 // again: on the 5120 -> 248 320 head at M = 7, 1024 blocks took 154.6 us
 // against 145.6 for the MFMA kernel (measured on MI355X), so larger N takes
-// the MFMA kernel.  K = 5120, waves: 2 CPL / 2 (two columns each), except 8
-// for M >= 5 once a block has 16 or more row quads (the first two columns to
-// some waves, one to the rest; two waves per SIMD; 5 again where 8 waves'
-// partials would not fit): measured at M = 7, the square (5 quads per block)
-// 6.55 us with 5 waves, 6.69 with 8; gate/up (34 quads) 22.5 with 5, 21.6
-// with 8; at M = 3 gate/up 20.1 with 5, 20.3 with 8.  K = 17408: 34 columns
+// the MFMA kernel.  K = 5120, waves: 2 CPL / 2 = 5 (two columns each) for
+// M <= 4; for M >= 5, 6 while a block has fewer than 16 row quads and 8 from
+// 16 on (the first 10 - W waves own two columns, the rest one; 5 again where
+// the partials would not fit).  Waves w and w + 4 share a SIMD, so with 5
+// waves SIMD 0 does four columns' work and the others two, while 6 and 8
+// waves load the SIMDs 3 / 3 / 2 / 2.  Measured (HIP-graph replay): the
+// square (5 quads per block) at M = 5 / 7 / 8 6.19 / 6.59 / 6.57 us with 5
+// waves, 5.93 / 6.26 / 6.21 with 6, 6.02 / 6.39 / 6.20 with 7 and 6.69 at
+// M = 7 with 8, but at M = 3 5.63 with 5 and 5.76 with 6; gate/up (34
+// quads) at M = 7 22.5 with 5, 21.6 with 8; at M = 3 20.1 with 5, 20.3 with
+// 8.  K = 17408: 34 columns
 // of x do not fit one workgroup's registers at two or three per wave, so
 // the row blocks are half as many and each has two workgroups, one per
 // K-slice of 17 columns (split-K partials in the workspace), of 9 waves: 8
@@ -294,7 +300,7 @@ bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
   if (S > 1) {
     W = 9;
   } else {
-    W = quads >= 16 && M >= 5 ? 8 : cpl;
+    W = M >= 5 ? (quads >= 16 ? 8 : 6) : cpl;
     if (W != cpl && xr_lds(M, fused, rows, W, jt) > kMaxLds) W = cpl;  // fewer partials per quad
   }
   if (!find_xr_kernel(M, cpl, epi, W, S)) return false;
