@@ -184,6 +184,9 @@ int rows_launch_bound(int MT, int cpl) { return (MT == 1 && cpl <= 8) ? 640 : 51
 // fused: one gate/up pair), else 4 (measured on MI355X: square 5120^2 with
 // 10 tasks per block 4.82 us at 8 waves, 5.04 at 10, 5.59 at 4; gate/up
 // 2 x 17408 x 5120 with 68 tasks per block 17.6 us at 4 waves, 17.9 at 8).
+// At M = 1 a block of 10 tasks takes 5 waves of two tasks each instead of 8
+// waves of which two have a second task: square 4.94 -> 4.88 us (at M = 2
+// 5.47 -> 5.73, so not there).
 bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
   if (M > kValuMaxM || epi == kEpiArgmax || K % 1024 != 0) return false;
 #ifdef W4A16_TUNING
@@ -201,7 +204,8 @@ bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
   pl = Plan{};
   pl.mfma = false;
   pl.lr = 32;
-  pl.W = per_block <= 16 ? 8 : 4;   // the kernel stages x with >= 4 waves
+  // the kernel stages x with >= 4 waves
+  pl.W = per_block > 16 ? 4 : (M == 1 && per_block == 10) ? 5 : 8;
   pl.LB = rows_launch_bound(M, cpl);
   pl.nrb = (int)nrb;
   pl.S = 1;
