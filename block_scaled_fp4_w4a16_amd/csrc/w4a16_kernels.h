@@ -1260,9 +1260,6 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
     load_task(qa, sa, 0);
     __builtin_amdgcn_sched_barrier(0);
 #ifdef W4A16_TRACE
-#ifdef W4A16_TRACE_XWAIT
-    __builtin_amdgcn_s_waitcnt(0);
-#endif
     t_issued = wall_clock64();
 #endif
     // g after the first loads: a scalar load's wait is lgkmcnt(0), which ahead
