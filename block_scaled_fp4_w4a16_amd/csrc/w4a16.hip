@@ -65,7 +65,8 @@ struct Plan {
   size_t lds;  // dynamic LDS bytes per workgroup
   size_t ws;   // workspace bytes (fp32 partials) when S > 1
   int rows_cpl; // > 0: the whole-row VALU kernel for K = 1024 * rows_cpl (S = 1)
-  int xr_cpl;   // > 0: the K-column MFMA kernel for K = 1024 * xr_cpl (S = 1)
+  int xr_cpl;   // > 0: the K-column MFMA kernel for K = 1024 * xr_cpl (S K-slices)
+  bool xr_ring; // the K-column kernel's ring variant (partials added per iteration)
 };
 
 // ---- kernel registry ---------------------------------------------------------
@@ -227,23 +228,31 @@ bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
 // / 23.9 / 24.3.)
 struct XrEntry {
   int M, cpl, epi, W, S;
+  bool ring;
   const void* fn;
 };
 #define W4A16_XE(MM, C, F, WW, SS) \
-  {MM, C, F, WW, SS, reinterpret_cast<const void*>(&k_gemm_xr<MM, C, F, WW, SS>)},
+  {MM, C, F, WW, SS, false, reinterpret_cast<const void*>(&k_gemm_xr<MM, C, F, WW, SS, false>)},
+#define W4A16_XR(MM, F, WW) \
+  {MM, 5, F, WW, 1, true, reinterpret_cast<const void*>(&k_gemm_xr<MM, 5, F, WW, 1, true>)},
+#define W4A16_XR_ALL(F) \
+  W4A16_XR(3, F, 5) W4A16_XR(4, F, 5) W4A16_XR(5, F, 8) W4A16_XR(6, F, 8) W4A16_XR(7, F, 8) W4A16_XR(8, F, 8)
 #define W4A16_XE_P2(C, F, WW, SS) \
   W4A16_XE(5, C, F, WW, SS) W4A16_XE(6, C, F, WW, SS) W4A16_XE(7, C, F, WW, SS) W4A16_XE(8, C, F, WW, SS)
 #define W4A16_XE_ALL(C, F, WW, SS) W4A16_XE(3, C, F, WW, SS) W4A16_XE(4, C, F, WW, SS) W4A16_XE_P2(C, F, WW, SS)
 const XrEntry kXrKernels[] = {W4A16_XE_ALL(5, kEpiPlain, 5, 1) W4A16_XE_ALL(5, kEpiSwiglu, 5, 1)
                               W4A16_XE_P2(5, kEpiPlain, 6, 1) W4A16_XE_P2(5, kEpiSwiglu, 6, 1)
                               W4A16_XE_P2(5, kEpiPlain, 8, 1) W4A16_XE_P2(5, kEpiSwiglu, 8, 1)
-                              W4A16_XE_P2(17, kEpiPlain, 9, 2)};
+                              W4A16_XE_P2(17, kEpiPlain, 9, 2)
+                              W4A16_XR_ALL(kEpiPlain) W4A16_XR_ALL(kEpiArgmax)};
+#undef W4A16_XR_ALL
+#undef W4A16_XR
 #undef W4A16_XE_ALL
 #undef W4A16_XE_P2
 #undef W4A16_XE
-const void* find_xr_kernel(int M, int cpl, int epi, int W, int S) {
+const void* find_xr_kernel(int M, int cpl, int epi, int W, int S, bool ring) {
   for (const XrEntry& e : kXrKernels)
-    if (e.M == M && e.cpl == cpl && e.epi == epi && e.W == W && e.S == S) return e.fn;
+    if (e.M == M && e.cpl == cpl && e.epi == epi && e.W == W && e.S == S && e.ring == ring) return e.fn;
   return nullptr;
 }
 // LDS bytes of k_gemm_xr<M, ..., W, S> for a row block of `rows` rows and a
@@ -252,8 +261,9 @@ const void* find_xr_kernel(int M, int cpl, int epi, int W, int S) {
 // 16-byte units), the floats per (quad, weight row) padded to 4 mod 8, as in
 // the kernel; at least the area the waves first stage their x in
 // (per column: P passes x 4 units x 64 lanes x 16 bytes)
-size_t xr_lds(int M, bool fused, long long rows, int W, int jt) {
-  const size_t quads = (size_t)((rows + 3) / 4) * (fused ? 2 : 1);
+size_t xr_lds(int M, bool fused, long long rows, int W, int jt, bool ring = false) {
+  size_t quads = (size_t)((rows + 3) / 4) * (fused ? 2 : 1);
+  if (ring && quads > 8 * kXrRingIterations) quads = 8 * kXrRingIterations;  // the ring's slots
   size_t js = (size_t)M * (4 * (size_t)W + (W % 2 == 0 ? 4 : 0));
   js += js % 8 == 0 ? 4 : 0;
   const size_t partials = quads * 4 * js * sizeof(float);
@@ -262,11 +272,14 @@ size_t xr_lds(int M, bool fused, long long rows, int W, int jt) {
 }
 
 // Plan for the K-column kernel, or false if it does not apply: one workgroup
-// per CU, whose partials must fit in LDS (K = 5120: N up to ~63 000 plain,
-// ~31 000 fused at M = 8, with 5 waves).  More workgroups would each load x
-// again: on the 5120 -> 248 320 head at M = 7, 1024 blocks took 154.6 us
-// against 145.6 for the MFMA kernel (measured on MI355X), so larger N takes
-// the MFMA kernel.  K = 5120, waves: 2 CPL / 2 = 5 (two columns each) for
+// per CU.  More workgroups would each load x again: on the 5120 -> 248 320
+// head at M = 7, 1024 blocks took 154.6 us against 145.6 for the MFMA kernel
+// (measured on MI355X).  Where a block's partials do not all fit in LDS (K =
+// 5120: N past ~63 000 plain at M = 8 with 5 waves), and for the argmax
+// epilogue, the ring variant adds them every two loop iterations instead
+// (plain and argmax; fused calls that large take the MFMA kernel): the head
+// at M = 3 / 5 / 7 / 8 in 114.6 / 122.7 / 127.1 / 130.0 us against 122.5 /
+// 139.7 / 143.1 / 144.0 for the MFMA kernel.  K = 5120, waves: 2 CPL / 2 = 5 (two columns each) for
 // M <= 4; for M >= 5, 6 while a block has fewer than 16 row quads and 8 from
 // 16 on (the first 10 - W waves own two columns, the rest one; 5 again where
 // the partials would not fit).  Waves w and w + 4 share a SIMD, so with 5
@@ -287,7 +300,7 @@ size_t xr_lds(int M, bool fused, long long rows, int W, int jt) {
 // at M = 3 / 4 (one pass of activation rows) 14.6 / 14.7 against 13.9 / 14.3,
 // so those stay on the MFMA kernel.
 bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
-  if (M < 3 || M > 8 || epi == kEpiArgmax || K % 1024 != 0) return false;
+  if (M < 3 || M > 8 || K % 1024 != 0) return false;
 #ifdef W4A16_TUNING
   if (g_override.enable) return false;
 #endif
@@ -301,14 +314,20 @@ bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
   const long long rows = N / nrb + (N % nrb > 0);
   const long long quads = (rows + 3) / 4 * (fused ? 2 : 1);
   int W;
+  bool ring = false;
   if (S > 1) {
     W = 9;
   } else {
     W = M >= 5 ? (quads >= 16 ? 8 : 6) : cpl;
     if (W != cpl && xr_lds(M, fused, rows, W, jt) > kMaxLds) W = cpl;  // fewer partials per quad
+    // the ring variant where the block's partials do not fit, and for argmax
+    if (epi == kEpiArgmax || xr_lds(M, fused, rows, W, jt) > kMaxLds) {
+      ring = true;
+      W = M >= 5 ? 8 : cpl;
+    }
   }
-  if (!find_xr_kernel(M, cpl, epi, W, S)) return false;
-  if (xr_lds(M, fused, rows, W, jt) > kMaxLds) return false;
+  if (!find_xr_kernel(M, cpl, epi, W, S, ring)) return false;
+  if (xr_lds(M, fused, rows, W, jt, ring) > kMaxLds) return false;
   pl = Plan{};
   pl.mfma = true;
   pl.lr = 1;
@@ -318,9 +337,13 @@ bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
   pl.S = S;
   pl.rq = N / (int)nrb;
   pl.rr = N % (int)nrb;
-  pl.lds = xr_lds(M, fused, pl.rq + (pl.rr > 0), W, jt);
-  pl.ws = S > 1 ? kCounterBytes + (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1) : 0;
+  pl.lds = xr_lds(M, fused, pl.rq + (pl.rr > 0), W, jt, ring);
+  if (epi == kEpiArgmax)  // arrival counter, then one candidate per row block and activation row
+    pl.ws = kCounterBytes + (size_t)pl.nrb * (size_t)M * 2 * sizeof(float);
+  else
+    pl.ws = S > 1 ? kCounterBytes + (size_t)S * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1) : 0;
   pl.xr_cpl = cpl;
+  pl.xr_ring = ring;
   return true;
 }
 
@@ -490,7 +513,7 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t
 
 hipError_t dispatch(const Plan& pl, int epi, hipStream_t s, const MatArgs& a) {
   if (pl.xr_cpl > 0) {
-    const void* fn = find_xr_kernel(a.M, pl.xr_cpl, epi, pl.W, pl.S);
+    const void* fn = find_xr_kernel(a.M, pl.xr_cpl, epi, pl.W, pl.S, pl.xr_ring);
     if (!fn || pl.W * 64 != pl.LB || a.K != 1024 * pl.xr_cpl || a.S != pl.S ||
         (pl.S > 1 && (a.part == nullptr || a.cnt == nullptr)))
       return hipErrorInvalidConfiguration;

@@ -1078,9 +1078,17 @@ __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows
 // kernel; gate/up 2 x 17408 x 5120 at M = 7 in 21.6 us with 8 waves (22.5
 // with 5) against 23.9.
 // ---------------------------------------------------------------------------
-template <int M, int CPL, int EPI, int W, int S>
+// Loop iterations (of two tasks) per combine in the ring variant below.
+// Measured on the 248 320 x 5120 head (graph replay): M = 5 / 7 / 8 128.2 /
+// 136.3 / 137.0 us at 1, 122.7 / 127.1 / 130.0 at 2, 123.3 / 128.5 / 136.5
+// at 4, against 139.7 / 143.1 / 144.0 for the MFMA kernel.
+constexpr int kXrRingIterations = 2;
+template <int M, int CPL, int EPI, int W, int S, bool RING>
 __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   constexpr bool FUSED = EPI == kEpiSwiglu;
+  constexpr bool ARGMAX = EPI == kEpiArgmax;
+  static_assert(!ARGMAX || (RING && S == 1), "the argmax epilogue runs on the ring variant");
+  static_assert(!RING || (S == 1 && !FUSED), "the ring variant: plain or argmax, no K split");
   constexpr int P = (M + 3) / 4;
   constexpr int K = 1024 * CPL;
   static_assert((2 * CPL) % S == 0, "K-slices of whole columns");
@@ -1096,6 +1104,15 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   // rows x 4 lane rows) of a partial then hit 16 distinct banks
   constexpr int JS = M * WR + ((M * WR) % 8 == 0 ? 4 : 0);
   static_assert(M >= 3 && M <= 8, "the K-column kernel serves 3 <= M <= 8");
+  // Ring variant: the partials of CI loop iterations (2 G CI quads) are added
+  // as soon as every wave has parked them, from two alternating halves of a
+  // ring of 4 G CI quads, so that the LDS holds that many quads whatever the
+  // block's rows.
+  constexpr int CI = kXrRingIterations;
+  constexpr int QI = 2 * G * CI;  // quads per combine
+  constexpr int RQ = 2 * QI;      // ring slots
+  static_assert(!RING || 4 * QI * M <= 64 * W, "one thread per output of a combine");
+  constexpr int MB = 4 * P;    // activation rows of the argmax candidates
   // 16-byte aligned (x units and partials are read as uint4 / float4), also
   // behind the static LDS of the split-K finish
   extern __shared__ uint4 red_lds[];
@@ -1123,6 +1140,33 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
 #ifdef W4A16_TRACE
   unsigned long long t_issued = 0, t_barrier = 0, t_first = 0, t_end = 0;
 #endif
+
+  // ring variant: the outputs of combine i (rows 4 QI i .. 4 QI i + 4 QI - 1
+  // of the block), one per thread; argmax: each thread keeps the best of the
+  // logits it has seen
+  float abv = -__builtin_inff();
+  int abi = kNoIndex;
+  auto ring_combine = [&](int i) {
+    const int o = tid;
+    if (o < 4 * QI * M) {
+      const int nl = o / M, m = o - nl * M;
+      const int n = 4 * QI * i + nl;
+      if (n < nrows) {
+        const float4* pg =
+            reinterpret_cast<const float4*>(red + (((n >> 2) & (RQ - 1)) * 4 + (n & 3)) * JS + m * WR);
+        float sg = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+          const float4 f = pg[w];
+          sg += (f.x + f.y) + (f.z + f.w);
+        }
+        if (ARGMAX)
+          argmax_take(abv, abi, sg * (1.0f / gv0), row_lo + n);
+        else
+          a.y[(size_t)m * a.N + row_lo + n] = f32_to_bf16(sg * (1.0f / gv0));
+      }
+    }
+  };
 
   // The wave's work for KJ = 1 or 2 columns (compile-time in each copy).
   auto body = [&](auto kj_count) {
@@ -1244,7 +1288,7 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
                 asm volatile("" : "+v"(vv[pp][r]));
               }
           if ((lane & 12) == 0) {
-            float* const dst = park + v * 4 * JS;
+            float* const dst = park + (RING ? (v & (RQ - 1)) : v) * 4 * JS;
 #pragma unroll
             for (int pp = 0; pp < P; ++pp)
 #pragma unroll
@@ -1305,6 +1349,13 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
       load_task(qa, sa, t + 2);
       __builtin_amdgcn_sched_barrier(0);
       if (t + 1 < ntasks) compute(qb, sb, t + 1);
+      if constexpr (RING) {
+        const int it = t >> 1;
+        if (it % CI == CI - 1 || t + 2 >= ntasks) {
+          lds_barrier();  // every wave has parked these iterations' quads
+          ring_combine(it / CI);
+        }
+      }
       t += 2;
     }
 #ifdef W4A16_TRACE
@@ -1320,6 +1371,39 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
       body(std::integral_constant<int, 1>{});
   }
 
+  if constexpr (RING) {
+    if constexpr (ARGMAX) {
+      lds_barrier();  // the last iteration's partials are read: red is free
+      float bv[MB];
+      int bi[MB];
+#pragma unroll
+      for (int mm = 0; mm < MB; ++mm) {
+        bv[mm] = -__builtin_inff();
+        bi[mm] = kNoIndex;
+      }
+      if (tid < 4 * QI * M) {
+        const int m = tid - (tid / M) * M;
+#pragma unroll
+        for (int mm = 0; mm < MB; ++mm)
+          if (mm == m) {
+            bv[mm] = abv;
+            bi[mm] = abi;
+          }
+      }
+      wg_argmax_rows<MB>(bv, bi, M, red, W);
+      if (tid < M) {
+        float* c = a.cand + ((size_t)rb * M + tid) * 2;
+        store_coherent(c, bv[0]);
+        store_coherent(c + 1, __int_as_float(bi[0]));
+      }
+      argmax_finish<MB>(a, a.cnt, gridDim.x, red, W);
+    }
+#ifdef W4A16_TRACE
+    W4A16_STAMP(t_done);
+    W4A16_TRACE_STORE(t_start, t_issued, t_barrier, t_first, t_end, t_done);
+#endif
+    return;
+  }
   lds_barrier();
   const float ig0 = 1.0f / gv0, ig1 = 1.0f / gv1;
   for (int o = tid; o < nrows * M; o += 64 * W) {

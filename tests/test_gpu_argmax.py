@@ -131,16 +131,19 @@ def test_run_to_run_identical():
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1].view(np.uint32), again[1].view(np.uint32))
 
 
-@pytest.mark.parametrize("M,K", [(3, 1024), (5, 1024), (13, 1024), (16, 5120), (29, 5120)])
-def test_ties_and_nan_rows_on_the_mfma_path(M, K):
-    """M >= 3 runs on the MFMA kernel, whose epilogue reduces every activation
-    row side by side (at K = 5120 and M > 12 after a K split, in the last
-    workgroup of each row block).  Exact arithmetic as above: for each
-    activation row m but the last, three weight rows hold m's largest possible
-    logit (codes +-6 with x[m]'s signs) and the smallest of them must win,
-    with the exact value; the last activation row holds a NaN, so all its
-    logits are NaN and its index is -1."""
-    N = 7000
+@pytest.mark.parametrize("M,K,N", [(3, 1024, 7000), (5, 1024, 7000), (13, 1024, 7000), (16, 5120, 7000),
+                                   (29, 5120, 7000), (3, 5120, 7000), (4, 5120, 7000), (6, 5120, 7000),
+                                   (8, 5120, 7000), (8, 5120, 100003)])
+def test_ties_and_nan_rows_on_the_mfma_path(M, K, N):
+    """M >= 3 runs on MFMA kernels that reduce every activation row side by
+    side: at K = 5120 and M <= 8 the K-column kernel's ring variant (each
+    thread keeps the best of the logits it adds, then the workgroup and the
+    last workgroup reduce), otherwise the general MFMA kernel (at K = 5120 and
+    M > 12 after a K split, in the last workgroup of each row block).  Exact
+    arithmetic as above: for each activation row m but the last, three weight
+    rows hold m's largest possible logit (codes +-6 with x[m]'s signs) and the
+    smallest of them must win, with the exact value; the last activation row
+    holds a NaN, so all its logits are NaN and its index is -1."""
     wq, ws, g, x, xi = exact_case(M, N, K, 30 + M)
     rng = np.random.default_rng(40 + M)
     planted = rng.choice(N, size=(M - 1, 3), replace=False)

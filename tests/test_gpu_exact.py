@@ -214,14 +214,23 @@ def test_k_column_kernel_two_slices_lds_limit_exact(N):
 @pytest.mark.parametrize("M,N,fused", [(8, 63488, False), (8, 63489, False), (7, 35000, True),
                                          (7, 40000, True)])
 def test_k_column_kernel_lds_limit_exact(M, N, fused):
-    """Either side of the largest N whose row blocks (one per CU) fit their
+    """Either side of the largest N whose row blocks (one per CU) fit all their
     partials in LDS: 63 488 rows plain at M = 8 (248 per block) still run the
-    K-column kernel (with 5 waves), 63 489 the MFMA kernel; likewise fused at
-    35 000 / 40 000."""
+    K-column kernel (with 5 waves), 63 489 its ring variant (partials added
+    per loop iteration); fused at 35 000 / 40 000 (the MFMA kernel past it)."""
     if fused:
         fused_exact(M, N, 5120, 1960 + N % 97, ctx=f"k-column limit fused N={N}")
     else:
         gemm_exact(M, N, 5120, 1950 + N % 97, ctx=f"k-column limit N={N}")
+
+
+@pytest.mark.parametrize("M,N", [(3, 200003), (5, 110000), (7, 248320)])
+def test_k_column_ring_variant_exact(M, N):
+    """Row blocks too large for all their partials in LDS run the K-column
+    kernel's ring variant: the quads of every two loop iterations are added as
+    soon as every wave has parked them.  Ragged last blocks and quads; the
+    248 320 rows of the head at M = 7."""
+    gemm_exact(M, N, 5120, 2400 + M + N % 89, "mant" if N % 2 else "pow2", ctx="k-column ring")
 
 
 # ---- one-hot sweep: every 32-input chunk position of K = 5120 -----------------
