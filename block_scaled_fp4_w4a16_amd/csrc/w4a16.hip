@@ -244,7 +244,8 @@ const XrEntry kXrKernels[] = {W4A16_XE_ALL(5, kEpiPlain, 5, 1) W4A16_XE_ALL(5, k
                               W4A16_XE_P2(5, kEpiPlain, 6, 1) W4A16_XE_P2(5, kEpiSwiglu, 6, 1)
                               W4A16_XE_P2(5, kEpiPlain, 8, 1) W4A16_XE_P2(5, kEpiSwiglu, 8, 1)
                               W4A16_XE_P2(17, kEpiPlain, 9, 2)
-                              W4A16_XR_ALL(kEpiPlain) W4A16_XR_ALL(kEpiArgmax)};
+                              W4A16_XR_ALL(kEpiPlain) W4A16_XR_ALL(kEpiSwiglu)
+                              W4A16_XR_ALL(kEpiArgmax)};
 #undef W4A16_XR_ALL
 #undef W4A16_XR
 #undef W4A16_XE_ALL
@@ -277,7 +278,8 @@ size_t xr_lds(int M, bool fused, long long rows, int W, int jt, bool ring = fals
 // (measured on MI355X).  Where a block's partials do not all fit in LDS (K =
 // 5120: N past ~63 000 plain at M = 8 with 5 waves), and for the argmax
 // epilogue, the ring variant adds them every two loop iterations instead
-// (plain and argmax; fused calls that large take the MFMA kernel): the head
+// (for gate/up, whose blocks fit, the ring was slower: 21.3 -> 22.1 us at
+// M = 7): the head
 // at M = 3 / 5 / 7 / 8 in 114.6 / 122.7 / 127.1 / 130.0 us against 122.5 /
 // 139.7 / 143.1 / 144.0 for the MFMA kernel.  K = 5120, waves: 2 CPL / 2 = 5 (two columns each) for
 // M <= 4; for M >= 5, 6 while a block has fewer than 16 row quads and 8 from

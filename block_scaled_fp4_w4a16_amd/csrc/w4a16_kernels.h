@@ -1088,7 +1088,7 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   constexpr bool FUSED = EPI == kEpiSwiglu;
   constexpr bool ARGMAX = EPI == kEpiArgmax;
   static_assert(!ARGMAX || (RING && S == 1), "the argmax epilogue runs on the ring variant");
-  static_assert(!RING || (S == 1 && !FUSED), "the ring variant: plain or argmax, no K split");
+  static_assert(!RING || S == 1, "the ring variant does not split K");
   constexpr int P = (M + 3) / 4;
   constexpr int K = 1024 * CPL;
   static_assert((2 * CPL) % S == 0, "K-slices of whole columns");
@@ -1111,7 +1111,8 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   constexpr int CI = kXrRingIterations;
   constexpr int QI = 2 * G * CI;  // quads per combine
   constexpr int RQ = 2 * QI;      // ring slots
-  static_assert(!RING || 4 * QI * M <= 64 * W, "one thread per output of a combine");
+  constexpr int RPC = FUSED ? 2 * QI : 4 * QI;  // output rows per combine (fused: QI / 2 pairs)
+  static_assert(!RING || RPC * M <= 64 * W, "one thread per output of a combine");
   constexpr int MB = 4 * P;    // activation rows of the argmax candidates
   // 16-byte aligned (x units and partials are read as uint4 / float4), also
   // behind the static LDS of the split-K finish
@@ -1141,29 +1142,41 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   unsigned long long t_issued = 0, t_barrier = 0, t_first = 0, t_end = 0;
 #endif
 
-  // ring variant: the outputs of combine i (rows 4 QI i .. 4 QI i + 4 QI - 1
-  // of the block), one per thread; argmax: each thread keeps the best of the
+  // ring variant: the outputs of combine i (rows RPC i .. RPC i + RPC - 1 of
+  // the block), one per thread; argmax: each thread keeps the best of the
   // logits it has seen
   float abv = -__builtin_inff();
   int abi = kNoIndex;
   auto ring_combine = [&](int i) {
     const int o = tid;
-    if (o < 4 * QI * M) {
+    if (o < RPC * M) {
       const int nl = o / M, m = o - nl * M;
-      const int n = 4 * QI * i + nl;
+      const int n = RPC * i + nl;
       if (n < nrows) {
+        const int vg = FUSED ? 2 * (n >> 2) : (n >> 2);
         const float4* pg =
-            reinterpret_cast<const float4*>(red + (((n >> 2) & (RQ - 1)) * 4 + (n & 3)) * JS + m * WR);
+            reinterpret_cast<const float4*>(red + ((vg & (RQ - 1)) * 4 + (n & 3)) * JS + m * WR);
         float sg = 0.0f;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
           const float4 f = pg[w];
           sg += (f.x + f.y) + (f.z + f.w);
         }
-        if (ARGMAX)
+        if (ARGMAX) {
           argmax_take(abv, abi, sg * (1.0f / gv0), row_lo + n);
-        else
+        } else if (FUSED) {
+          const float4* pu =
+              reinterpret_cast<const float4*>(red + (((vg + 1) & (RQ - 1)) * 4 + (n & 3)) * JS + m * WR);
+          float su = 0.0f;
+#pragma unroll
+          for (int w = 0; w < W; ++w) {
+            const float4 f = pu[w];
+            su += (f.x + f.y) + (f.z + f.w);
+          }
+          a.y[(size_t)m * a.N + row_lo + n] = f32_to_bf16(silu(sg * (1.0f / gv0)) * (su * (1.0f / gv1)));
+        } else {
           a.y[(size_t)m * a.N + row_lo + n] = f32_to_bf16(sg * (1.0f / gv0));
+        }
       }
     }
   };
@@ -1381,7 +1394,7 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
         bv[mm] = -__builtin_inff();
         bi[mm] = kNoIndex;
       }
-      if (tid < 4 * QI * M) {
+      if (tid < RPC * M) {
         const int m = tid - (tid / M) * M;
 #pragma unroll
         for (int mm = 0; mm < MB; ++mm)

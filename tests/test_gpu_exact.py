@@ -217,7 +217,7 @@ def test_k_column_kernel_lds_limit_exact(M, N, fused):
     """Either side of the largest N whose row blocks (one per CU) fit all their
     partials in LDS: 63 488 rows plain at M = 8 (248 per block) still run the
     K-column kernel (with 5 waves), 63 489 its ring variant (partials added
-    per loop iteration); fused at 35 000 / 40 000 (the MFMA kernel past it)."""
+    per loop iteration); likewise fused at 35 000 / 40 000."""
     if fused:
         fused_exact(M, N, 5120, 1960 + N % 97, ctx=f"k-column limit fused N={N}")
     else:
