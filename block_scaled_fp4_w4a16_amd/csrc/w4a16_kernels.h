@@ -1072,11 +1072,15 @@ __global__ void __launch_bounds__((MT == 1 && CPL <= 8) ? 640 : 512) k_gemm_rows
 // the current one is computed (the whole-row kernel's loop).  With S > 1 K-
 // slices, workgroup (rb, ks) covers columns ks JT .. ks JT + JT - 1 of row
 // block rb and parks its sums in the split-K partials; the row block's last
-// workgroup adds the slices in order (splitk_finish).
+// workgroup adds the slices in order (splitk_finish).  The ring variant
+// (RING) adds the partials every few loop iterations instead of after the
+// loop, so that a row block of any size fits the LDS; it also serves the
+// argmax epilogue (each thread keeps the best logit it adds, then the
+// workgroup's and the grid's candidates are reduced).
 // Measured on MI355X (HIP-graph replay, 64 / 32 cycled copies): 5120 x 5120
-// at M = 7 in 6.55 us with 5 waves (6.69 with 8) against 7.99 for the MFMA
-// kernel; gate/up 2 x 17408 x 5120 at M = 7 in 21.6 us with 8 waves (22.5
-// with 5) against 23.9.
+// at M = 7 in 6.3 us with 6 waves (6.6 with 5, 6.7 with 8) against 7.99 for
+// the MFMA kernel; gate/up 2 x 17408 x 5120 at M = 7 in 21.0-21.6 us with 8
+// waves (22.5 with 5) against 23.9.
 // ---------------------------------------------------------------------------
 // Loop iterations (of two tasks) per combine in the ring variant below.
 // Measured on the 248 320 x 5120 head (graph replay): M = 5 / 7 / 8 128.2 /
