@@ -193,6 +193,11 @@ def test_argmax_argument_checks(lib):
     assert w4.workspace_size_argmax(13, 1000, 5120) >= 4096 + 2 * 13 * 1000 * 4
     assert 4096 < w4.workspace_size_argmax(12, 1000, 5120) < 4096 + 12 * 1000 * 4
     assert w4.workspace_size_argmax(1, 248320, 5120) >= 4096 + 8
+    # the head at 3 <= M <= 8 runs the K-column kernel's ring variant, one row
+    # block per CU (256 here, without a device): the arrival counter, then one
+    # (value, index) candidate per row block and activation row
+    for M in range(3, 9):
+        assert w4.workspace_size_argmax(M, 248320, 5120) == 4096 + 256 * M * 2 * 4, M
     assert w4.workspace_size_argmax(16, 64, 17408) >= 4096 + 16 * 64 * 4
     assert w4.workspace_size_argmax(2, 64, 65536) == 0         # M <= 2 takes no K split
 
