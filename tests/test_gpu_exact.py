@@ -293,6 +293,25 @@ def test_head_argmax_exact_winner(M):
     assert int(work[:4096].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("M,N", [(3, 1), (5, 3), (8, 257), (6, 5120)])
+def test_argmax_ring_small_n_exact_winner(M, N):
+    """The K-column kernel's argmax at N below and just past the CU count (row
+    blocks of one or two rows, or none): exact logits, unique winner."""
+    K = 5120
+    wq, ws, g, x = exact.exact_gemm_case(1480 + M + N, M, N, K)
+    say(f"[exact argmax ring] M={M} N={N} K={K}")
+    work = torch.zeros(w4.workspace_size_argmax(M, N, K), dtype=torch.uint8, device="cuda")
+    ref, a = oracle.gemm(wq, ws, g, x, M, N, K, nthreads=NTHREADS)
+    exact.assert_exact_regime(a, g, "pow2", "argmax ring")
+    want_idx = np.argmax(ref, axis=1)
+    for call in range(2):
+        idx, val = w4.gemm_argmax(d_u8(wq), d_u8(ws), d_g(g), d_bf16(x), workspace=work)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), want_idx), (call, idx.cpu().numpy(), want_idx)
+        assert np.array_equal(val.cpu().numpy().astype(np.float64), ref[np.arange(M), want_idx]), call
+        assert int(work[:4096].count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("M,N", [(13, 4099), (16, 4099), (24, 1031), (32, 4099), (16, 65536)])
 def test_argmax_with_k_split_exact_winner(M, N):
     """From M = 13 at K = 5120 the x rows exceed the LDS next to the scratch,
