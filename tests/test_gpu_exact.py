@@ -224,6 +224,13 @@ def test_k_column_kernel_lds_limit_exact(M, N, fused):
         gemm_exact(M, N, 5120, 1950 + N % 97, ctx=f"k-column limit N={N}")
 
 
+@pytest.mark.parametrize("M,N", [(3, 90000), (4, 90001)])
+def test_k_column_ring_variant_fused_exact(M, N):
+    """Fused calls past the LDS limit at M <= 4 (5 waves): the ring variant
+    pairs each gate quad with its up quad within a combine."""
+    fused_exact(M, N, 5120, 2450 + M, ctx="k-column ring fused")
+
+
 @pytest.mark.parametrize("M,N", [(3, 200003), (5, 110000), (7, 248320)])
 def test_k_column_ring_variant_exact(M, N):
     """Row blocks too large for all their partials in LDS run the K-column
