@@ -14,9 +14,11 @@ M = 7, a verify block of 6 drafts + 1) on the configurations that define
 them: the square projection at M = 7, the fused gate/up + SwiGLU (K = 5120,
 2 x N = 17408, 32 layer copies) and the down projection (K = 17408,
 N = 5120, 32 copies), each at M = 1 and 7 with median and minimum over 5
-timed windows; the oracle timed on the host (one thread and all cores); and
-an achievable-read calibration.  `--extra` adds the down projection at
-M = 2, 4, 8, 16, 32 and the MLP block; `--tower` the full-tower decode sweep.
+timed windows; the oracle timed on the host (one thread and all cores); an
+achievable-read calibration; and the full-tower decode sweep (64 layers of
+gate/up, down and q/k/v/o plus the 5120 -> 248320 head, M = 1 and 7; skip it
+with --no-tower).  `--extra` adds the down projection at M = 2, 4, 8, 16, 32
+and the MLP block.
 
 Inputs are resident in HBM before any timed region starts.
 """
@@ -765,7 +767,9 @@ def main():
     ap.add_argument("--extra", action="store_true",
                     help="also time the down projection at M = 2, 4, 8, 16, 32 and the MLP block")
     ap.add_argument("--tower", action="store_true",
-                    help="also time the full-tower decode sweep (64 layers + head, 14.1 GB, M = 1 and 7)")
+                    help="(the default) time the full-tower decode sweep (64 layers + head, 14.1 GB, "
+                         "M = 1 and 7)")
+    ap.add_argument("--no-tower", action="store_true", help="skip the full-tower decode sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-calibration", action="store_true",
                     help="skip the achievable-read-bandwidth calibration")
@@ -827,7 +831,7 @@ def main():
             kind = next((k for k in cal["call_sized"] if name.startswith(k + "_M")), None)
             if kind is not None and "us_per_call" in rec:
                 rec["frac_of_call_sized_read"] = round(cal["call_sized"][kind]["us_per_call"] / rec["us_per_call"], 4)
-    tower = bench_tower(dev, stream) if args.tower else None
+    tower = None if args.no_tower else bench_tower(dev, stream)
     del sq
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     if tower is not None and not args.no_cpu_baseline:
