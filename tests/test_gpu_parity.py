@@ -253,6 +253,19 @@ def test_nan_scale_propagates_to_its_row_only_at_k5120(M):
     assert not np.isnan(np.delete(yf, 130, axis=1)).any()
 
 
+def test_nan_scale_propagates_to_its_row_only_on_the_ring():
+    """The same through the K-column kernel's ring variant (110 000 rows at
+    M = 5: partials added every two loop iterations): the NaN row lies in the
+    middle of a row block's walk."""
+    M, N, K = 5, 110000, 5120
+    wq = synth.random_bytes(28, (N, K // 2))
+    ws = (synth.random_bytes(29, (N, K // 16)) & np.uint8(0x37)) | np.uint8(0x08)   # finite, positive
+    ws[70001, 77] = 0x7F
+    y = run_gemm(wq, ws, np.float32(512.0), synth.activations(30, M, K), M, N, K)
+    assert np.isnan(y[:, 70001]).all()
+    assert not np.isnan(np.delete(y, 70001, axis=1)).any()
+
+
 def test_zero_weights_give_zero():
     for M in (1, 5):
         N, K = 50, 256
