@@ -219,9 +219,9 @@ bool plan_rows(int M, int N, int K, int epi, Plan& pl) {
 }
 
 // K-column MFMA kernels with x in registers (k_gemm_xr), 3 <= M <= 8 at
-// K = 5120 (CPL = 5; plain and SwiGLU epilogues), and 5 <= M <= 8 at K =
-// 17408 (CPL = 17, the down projection; plain, in two K-slices of 17
-// columns); other shapes take the MFMA kernel.  (Measured on MI355X against the MFMA kernel,
+// K = 5120 (CPL = 5; plain, SwiGLU and argmax epilogues) and at K = 17408
+// (CPL = 17, the down projection; plain, in two K-slices of 17 columns);
+// other shapes take the MFMA kernel.  (Measured on MI355X against the MFMA kernel,
 // HIP-graph replay: 5120 x 5120 at M = 3, 4, 5, 7, 8: 5.55 / 5.61 / 6.43 /
 // 6.60 / 6.68 us against 7.02 / 7.07 / 7.85 / 7.99 / 8.01; gate/up 2 x 17408
 // x 5120 at M = 4, 5, 7, 8: 20.2 / 21.2 / 21.6 / 21.8 us against 22.1 / 23.3
@@ -243,7 +243,7 @@ struct XrEntry {
 const XrEntry kXrKernels[] = {W4A16_XE_ALL(5, kEpiPlain, 5, 1) W4A16_XE_ALL(5, kEpiSwiglu, 5, 1)
                               W4A16_XE_P2(5, kEpiPlain, 6, 1) W4A16_XE_P2(5, kEpiSwiglu, 6, 1)
                               W4A16_XE_P2(5, kEpiPlain, 8, 1) W4A16_XE_P2(5, kEpiSwiglu, 8, 1)
-                              W4A16_XE_P2(17, kEpiPlain, 9, 2)
+                              W4A16_XE_ALL(17, kEpiPlain, 9, 2)
                               W4A16_XR_ALL(kEpiPlain) W4A16_XR_ALL(kEpiSwiglu)
                               W4A16_XR_ALL(kEpiArgmax)};
 #undef W4A16_XR_ALL
@@ -297,10 +297,9 @@ size_t xr_lds(int M, bool fused, long long rows, int W, int jt, bool ring = fals
 // K-slice of 17 columns (split-K partials in the workspace), of 9 waves: 8
 // of two columns and one of one.  (16 waves, one of two columns and 15 of
 // one, would leave 128 VGPRs per wave: the two-column wave spills.)
-// Measured, 5120 x 17408 at M = 5 / 6 / 7 / 8: 15.1 / 15.5 / 15.5 / 15.9 us
-// against 16.5 / 16.9 / 17.0 / 17.3 for the MFMA kernel (also two K-slices);
-// at M = 3 / 4 (one pass of activation rows) 14.6 / 14.7 against 13.9 / 14.3,
-// so those stay on the MFMA kernel.
+// Measured, 5120 x 17408 at M = 3 / 4 / 5 / 7 / 8: 13.4 / 13.8 / 13.9 / 14.3 /
+// 14.4 us against 14.1 / 14.4 / 16.5 / 17.0 / 17.3 for the MFMA kernel (also
+// two K-slices from M = 5).
 bool plan_xr(int M, int N, int K, int epi, Plan& pl) {
   if (M < 3 || M > 8 || K % 1024 != 0) return false;
 #ifdef W4A16_TUNING

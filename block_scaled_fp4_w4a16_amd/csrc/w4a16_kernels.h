@@ -1099,7 +1099,11 @@ __global__ void __launch_bounds__(64 * W) k_gemm_xr(MatArgs a) {
   constexpr int JT = 2 * CPL / S;  // chunk columns of 16 chunks in this K-slice
   constexpr int N2 = JT - W;       // waves 0..N2-1 own two columns, the rest one
   static_assert(W <= JT && JT <= 2 * W, "every wave owns one or two columns");
-  constexpr int G = 2;           // quads per task
+  // quads per task: 2; 1 for the two-slice down blocks (10 quads: finer tasks
+  // keep more of the walk overlapped; measured down M = 5 / 7 / 8 14.9 / 15.5
+  // / 15.9 us at 2, 13.9 / 14.6 / 15.1 at 1, while the square and gate/up
+  // are 3-4 % slower at 1 and 5-9 % at 3)
+  constexpr int G = S > 1 ? 1 : 2;
   // floats per (quad, weight row, activation row): 4 W partials, padded to an
   // odd number of 16-byte units, so that the combine's float4 reads of
   // consecutive activation rows (consecutive threads) spread over the banks

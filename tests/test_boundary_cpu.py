@@ -121,9 +121,9 @@ def test_workspace_sizes(lib):
         S, counters = divmod(size - 4096, M * N * 4 * (2 if fused else 1))
         assert S >= 2 and counters == 0, (M, N, K, size)
     assert w4.workspace_size(33, 64, 256) == 0            # unsupported shape: 0
-    # the down projection at 5 <= M <= 8 runs the K-column kernel in exactly two
+    # the down projection at 3 <= M <= 8 runs the K-column kernel in exactly two
     # K-slices (one workgroup per slice and row block)
-    for M in (5, 6, 7, 8):
+    for M in (3, 4, 5, 6, 7, 8):
         assert w4.workspace_size(M, 5120, 17408) == 4096 + 2 * M * 5120 * 4, M
     # the MLP block's workspace holds what either launch plan of each phase needs
     for M in (1, 3, 4, 7, 8, 16):

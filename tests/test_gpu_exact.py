@@ -196,10 +196,9 @@ def test_k_column_kernel_eight_waves_fused_exact(M):
 @pytest.mark.parametrize("M", [3, 4, 5, 6, 7, 8])
 @pytest.mark.parametrize("N", [1, 3, 129, 5121])
 def test_k_column_kernel_two_slices_exact(M, N):
-    """K = 17 408 at M >= 5: two workgroups per row block, one per K-slice of
-    17 columns, added by the row block's last workgroup (M = 3, 4: the MFMA
-    kernel); fewer rows than row blocks, a ragged row block and a ragged last
-    quad."""
+    """K = 17 408: two workgroups per row block, one per K-slice of 17
+    columns, added by the row block's last workgroup; fewer rows than row
+    blocks, a ragged row block and a ragged last quad."""
     gemm_exact(M, N, 17408, 2200 + 11 * M + N % 97, "mant" if (M + N) % 2 else "pow2",
                ctx="k-column two slices")
 
