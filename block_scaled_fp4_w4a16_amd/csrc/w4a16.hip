@@ -67,6 +67,8 @@ struct Plan {
   int rows_cpl; // > 0: the whole-row VALU kernel for K = 1024 * rows_cpl (S = 1)
   int xr_cpl;   // > 0: the K-column MFMA kernel for K = 1024 * xr_cpl (S K-slices)
   bool xr_ring; // the K-column kernel's ring variant (partials added per iteration)
+  int wide_mt;  // > 0: the wide kernel for M <= 8 * wide_mt (rq = tiles of 32 rows per row block)
+  int wide_steps; // ... and its K-slice length in steps of 256 inputs (the last slice may be shorter)
 };
 
 // ---- kernel registry ---------------------------------------------------------
@@ -272,6 +274,96 @@ size_t xr_lds(int M, bool fused, long long rows, int W, int jt, bool ring = fals
   return partials > x_stage ? partials : x_stage;
 }
 
+// ---- wide kernel (9 <= M <= 32) ----------------------------------------------
+struct WideEntry {
+  int mt, epi;
+  const void* fn;
+};
+#define W4A16_WE(MT, F) {MT, F, reinterpret_cast<const void*>(&k_gemm_wide<MT, F>)},
+const WideEntry kWideKernels[] = {W4A16_WE(4, kEpiPlain) W4A16_WE(4, kEpiSwiglu)};
+#undef W4A16_WE
+const void* find_wide_kernel(int mt, int epi) {
+  for (const WideEntry& e : kWideKernels)
+    if (e.mt == mt && e.epi == epi) return e.fn;
+  return nullptr;
+}
+// From 17 rows on (measured on MI355X by HIP-graph replay, M = 9 / 16 / 24 /
+// 32, wide kernel against the 4x4x4 MFMA kernel: down 5120 x 17408 22.5 /
+// 23.2 / 26.6 / 27.4 us against 19.9 / 24.0 / 36.1 / 47.8; gate/up 2 x 17408
+// x 5120 43.2 / 45.0 / 48.4 / 51.4 against 28.1 / 42.1 / 56.3 / 83.1; the
+// square 5120^2 14.1 / 14.7 / 17.6 / 18.0 against 9.1 / 13.0 / 16.0 / 23.3).
+// Below that the wide kernel's fixed costs (x staging, partial sums and their
+// finish) outweigh what it saves.
+constexpr int kWideMinM = 17;
+// LDS bytes of k_gemm_wide<mt, ...> for a K-slice of `steps` steps of 256
+// inputs: 8 * mt rows of steps * 32 units of 16 bytes, plus one unit per row
+size_t wide_lds(int mt, int steps) { return (size_t)8 * mt * ((size_t)steps * 32 + 1) * 16; }
+
+// Plan for the wide kernel, or false if it does not apply.  Row blocks of 8
+// tiles (one per wave: two waves per SIMD, so that one runs while the other
+// waits for memory); K-slices of u x 512 inputs (the slice's x must fit in
+// LDS).  Among every u, the plan with the least estimated time: the busiest
+// SIMD's tile work (tiles x 512 inputs, ~1.2 us each) plus the split-K
+// partials written and read back (at ~4 TB/s); ties go to fewer slices, then
+// to fewer rounds of workgroups.
+bool plan_wide(int M, int N, int K, int epi, Plan& pl) {
+  if (M < kWideMinM || M > 32 || epi == kEpiArgmax || K % 512 != 0) return false;
+#ifdef W4A16_TUNING
+  if (g_override.enable) return false;
+#endif
+  const int mt = 4;
+  const bool fused = epi == kEpiSwiglu;
+  if (!find_wide_kernel(mt, epi)) return false;
+  const int cus = cu_count();
+  const long long T = ((long long)N + 31) / 32;
+  const int units = K / 512;
+  const double unit_us = 1.2 * (fused ? 2 : 1);
+  double best = 1e30;
+  int bW = 0, bu = 0, bS = 0;
+  long long bnrb = 0, brounds = 0;
+  for (int W = 8; W <= 8; ++W) {  // two waves per SIMD (one hides the other's waits)
+    const long long nrb = (T + W - 1) / W;
+    for (int u = 1; u <= units; ++u) {
+      const size_t lds = wide_lds(mt, 2 * u);
+      if (lds > kMaxLds) break;
+      const int S = (units + u - 1) / u;
+      if (S > 1 && nrb > kMaxSplitRowBlocks) continue;
+      long long per_cu = (long long)(kMaxLds / lds);
+      const long long wave_cap = W <= 4 ? 2 : 1;  // two waves per SIMD
+      if (per_cu > wave_cap) per_cu = wave_cap;
+      const long long wgs = nrb * S;
+      const long long wg_per_cu = (wgs + cus - 1) / cus;
+      const long long rounds = (wgs + cus * per_cu - 1) / (cus * per_cu);
+      const double load = (double)((wg_per_cu * W + 3) / 4) * u;
+      const double part = S > 1 ? 2.0 * S * M * (double)N * 4 * (fused ? 2 : 1) : 0.0;
+      const double t = load * unit_us + part / 4e6;
+      if (t < best - 1e-9 || (t < best + 1e-9 && (S < bS || (S == bS && rounds < brounds)))) {
+        best = t;
+        bW = W;
+        bu = u;
+        bS = S;
+        bnrb = nrb;
+        brounds = rounds;
+      }
+    }
+  }
+  if (bW == 0) return false;
+  pl = Plan{};
+  pl.mfma = true;
+  pl.lr = 1;
+  pl.W = bW;
+  pl.LB = 512;
+  pl.nrb = (int)bnrb;
+  pl.S = bS;
+  pl.rq = bW;  // tiles per row block
+  pl.rr = 0;
+  pl.lds = wide_lds(mt, 2 * bu);
+  pl.ws = bS > 1 ? kCounterBytes + (size_t)bS * (size_t)M * (size_t)N * sizeof(float) * (fused ? 2 : 1) : 0;
+  pl.wide_mt = mt;
+  pl.wide_steps = 2 * bu;
+  return true;
+}
+
 // Plan for the K-column kernel, or false if it does not apply: one workgroup
 // per CU.  More workgroups would each load x again: on the 5120 -> 248 320
 // head at M = 7, 1024 blocks took 154.6 us against 145.6 for the MFMA kernel
@@ -360,6 +452,7 @@ Plan plan_gemm(int M, int N, int K, int epi, bool rows_ok = true, bool xr_ok = t
     Plan r;
     if (rows_ok && plan_rows(M, N, K, epi, r)) return r;
     if (xr_ok && plan_xr(M, N, K, epi, r)) return r;
+    if (xr_ok && plan_wide(M, N, K, epi, r)) return r;
   }
   const bool fused = epi == kEpiSwiglu;
   Plan pl{};
@@ -513,6 +606,16 @@ hipError_t launch(const void* fn, dim3 grid, dim3 block, size_t lds, hipStream_t
 }
 
 hipError_t dispatch(const Plan& pl, int epi, hipStream_t s, const MatArgs& a) {
+  if (pl.wide_mt > 0) {
+    const void* fn = find_wide_kernel(pl.wide_mt, epi);
+    if (!fn || pl.W < 1 || pl.W > 8 || a.M > 8 * pl.wide_mt || a.K % 512 != 0 ||
+        pl.wide_steps % 2 != 0 || a.CRS != pl.wide_steps || a.S != pl.S ||
+        (long long)pl.S * pl.wide_steps < a.K / 256 || (long long)(pl.S - 1) * pl.wide_steps >= a.K / 256 ||
+        (long long)pl.nrb * pl.rq * 32 < a.N || pl.lds != wide_lds(pl.wide_mt, pl.wide_steps) ||
+        (pl.S > 1 && (a.part == nullptr || a.cnt == nullptr)))
+      return hipErrorInvalidConfiguration;
+    return launch(fn, dim3((unsigned)pl.nrb, (unsigned)pl.S), dim3((unsigned)(pl.W * 64)), pl.lds, s, a);
+  }
   if (pl.xr_cpl > 0) {
     const void* fn = find_xr_kernel(a.M, pl.xr_cpl, epi, pl.W, pl.S, pl.xr_ring);
     if (!fn || pl.W * 64 != pl.LB || a.K != 1024 * pl.xr_cpl || a.S != pl.S ||
@@ -555,6 +658,7 @@ w4a16_status_t check_shape(int M, int N, int K) {
 // give the same bits).
 int split_rows(int M, int N, int K, int epi) {
   if (M <= 16 || epi == kEpiArgmax) return 0;
+  if (plan_gemm(M, N, K, epi).wide_mt > 0) return 0;  // the wide kernel takes all 32 rows at once
   int m1 = (M / 2 + 3) / 4 * 4;
   if (m1 > 16) m1 = 16;
   return plan_gemm(M, N, K, epi).S >= (epi == kEpiSwiglu ? 4 : 16) ? m1 : 0;
@@ -577,8 +681,8 @@ void prepare(MatArgs& a, const Plan& pl, int* cnt, float* part) {
   a.rr = pl.rr;
   a.kmax = pl.kmax;
   a.S = pl.S;
-  a.CRS = (a.K >> 5) / pl.S;
-  const int cpl = pl.mfma ? (a.CRS + 15) / 16 : a.CRS / pl.lr;
+  a.CRS = pl.wide_mt > 0 ? pl.wide_steps : (a.K >> 5) / pl.S;
+  const int cpl = pl.wide_mt > 0 ? 1 : pl.mfma ? (a.CRS + 15) / 16 : a.CRS / pl.lr;
   a.rW = 1.0f / (float)pl.W;
   a.rCPL = 1.0f / (float)cpl;
   a.rUPR = 1.0f / (float)(a.CRS * 4);
@@ -687,7 +791,8 @@ MlpPlan plan_mlp(int M, int H, int F) {
   // the two paths give the same bits.
   const Plan &a = mp.p1, &b = mp.p2;
   if (a.mfma != b.mfma || a.W != b.W || a.LB != b.LB || a.D != b.D ||
-      (size_t)M * F * 2 >= ((size_t)1 << 31) || mp.l1.xr_cpl > 0 || mp.l2.xr_cpl > 0)
+      (size_t)M * F * 2 >= ((size_t)1 << 31) || mp.l1.xr_cpl > 0 || mp.l2.xr_cpl > 0 ||
+      mp.l1.wide_mt > 0 || mp.l2.wide_mt > 0)
     return mp;
   const int rows = a.mfma ? (M + 3) / 4 : M;
   for (const MlpKernEntry& e : kMlpKernels)
@@ -1100,6 +1205,14 @@ __attribute__((visibility("default"))) void w4a16_tuning_plan(int M, int N, int 
   const long long v[12] = {pl.mfma, pl.lr, pl.D, pl.W, pl.LB, pl.nrb, pl.S,
                            pl.rq, pl.rr, pl.kmax, (long long)pl.lds, (long long)pl.ws};
   for (int i = 0; i < 12; ++i) out[i] = v[i];
+}
+// Tuning builds only: the wide kernel's part of the plan, as 7 ints
+// {wide_mt, wide_steps, W, nrb, S, lds, ws} (wide_mt = 0: another kernel).
+__attribute__((visibility("default"))) void w4a16_tuning_plan_wide(int M, int N, int K, int epi,
+                                                                    long long* out) {
+  const Plan pl = plan_gemm(M, N, K, epi);
+  const long long v[7] = {pl.wide_mt, pl.wide_steps, pl.W, pl.nrb, pl.S, (long long)pl.lds, (long long)pl.ws};
+  for (int i = 0; i < 7; ++i) out[i] = v[i];
 }
 #endif
 #ifdef W4A16_TRACE

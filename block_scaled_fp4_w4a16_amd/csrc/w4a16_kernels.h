@@ -1809,6 +1809,263 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Wide kernel, 17 <= M <= 32: one 32 x 32 x 16 bf16 MFMA per 16-input scale
+// block, accumulating over the whole K-slice.  An E2M1 value times an E4M3
+// scale has at most 6 significant bits, so each weight times its block scale
+// is exact in bf16: the weights enter the MFMA already scaled (fp32 products
+// packed to bf16 without rounding) and no per-block work waits for an MFMA
+// result.  The global scale divides the sum once, in the epilogue.
+//
+// v_mfma_f32_32x32x16_bf16: lane l holds A[l % 32][8 * (l / 32) + e] and
+// B[8 * (l / 32) + e][l % 32] (e = 0..7) and receives C[i][l % 32] in
+// register r, i = 8 * (r / 4) + 4 * (l / 32) + r % 4.  Here A is x (rows =
+// activation rows; rows >= M are zero), B the scaled weights of 32
+// consecutive rows (columns = weight rows).
+//
+// A wave owns a tile of 32 weight rows over the workgroup's K-slice and walks
+// it in steps of 256 inputs: the two lanes of row n read that row's 128 bytes
+// of codes (one whole cache line; lane g the 16-byte pieces 2j + g, j = 0..3,
+// so each load instruction takes 32 contiguous bytes per row) and its 16
+// scale bytes.  Per piece pair j, two cross-half lane swaps leave lane g with
+// half g (8 inputs, one dword of codes) of each of blocks 4j..4j+3, which is
+// the MFMA's B operand after four E2M1 -> bf16 conversions.  The x slice is
+// staged in LDS as [row][k] with a 16-byte pad per row; lane (m, g) reads its
+// 8 inputs of a block with one 16-byte LDS read.  A workgroup of W waves owns
+// a row block of a.rq tiles (wave w: tiles w, w + W, ...) and K-slice
+// blockIdx.y of a.CRS steps (the last slice may be shorter).  With S > 1 the slices' fp32 sums go to the
+// split-K partials and the row block's last workgroup adds them in slice
+// order (splitk_finish).  Fused gate/up: every tile runs the gate and the up
+// rows side by side on the same x reads.
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+// two E2M1 codes (byte B of w) times the block scale s, as two bf16 in one
+// dword: the products are exact in fp32 and in bf16
+template <int B>
+W4A16_DEV uint32_t scaled_bf16x2(uint32_t w, float s) {
+  const f32x2_t v = fp4x2_to_f32x2<B>(w);
+  const bf16x2_t r = {(__bf16)(v[0] * s), (__bf16)(v[1] * s)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+// Split-K finish of the wide kernel: as splitk_finish (the row block's last
+// workgroup adds the slices in order 0..S-1), but each thread issues the
+// loads of G outputs x 8 slices before adding any of them, so that the
+// finishing workgroup waits for one far round trip per 8 slices instead of
+// one per output.
+template <bool FUSED>
+W4A16_DEV void wide_finish(const MatArgs& a, int rb, int row_lo, int nrows, float ig0, float ig1) {
+  __shared__ int is_last;
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int before = __hip_atomic_fetch_add(a.cnt + rb, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = before == a.S - 1;
+    if (is_last) __hip_atomic_store(a.cnt + rb, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  constexpr int G = FUSED ? 4 : 8;  // outputs per thread per pass
+  const int S = a.S, NT = blockDim.x, tot = nrows * a.M;
+  const size_t MN = (size_t)a.M * a.N;
+  const float rn = 1.0f / (float)nrows;
+  for (int o0 = threadIdx.x; o0 < tot; o0 += G * NT) {
+    size_t idx[G];
+    float v[G], u[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+      const int o = min(o0 + q * NT, tot - 1);  // past the end: repeat a valid output
+      const int m = div_small(o, nrows, rn), n = o - m * nrows;
+      idx[q] = (size_t)m * a.N + row_lo + n;
+      v[q] = 0.0f;
+      u[q] = 0.0f;
+    }
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float t[G][8], tu[G][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const size_t off = (size_t)min(s0 + j, S - 1) * MN;
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+          t[q][j] = load_coherent(a.part + off + idx[q]);
+          if (FUSED) tu[q][j] = load_coherent(a.part + (size_t)S * MN + off + idx[q]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < S) {
+#pragma unroll
+          for (int q = 0; q < G; ++q) {
+            v[q] += t[q][j];
+            if (FUSED) u[q] += tu[q][j];
+          }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+      if (o0 + q * NT < tot) {
+        if (FUSED) a.y[idx[q]] = f32_to_bf16(silu(v[q] * ig0) * (u[q] * ig1));
+        else a.y[idx[q]] = f32_to_bf16(v[q] * ig0);
+      }
+  }
+}
+
+template <int MT, int EPI>
+__global__ void __launch_bounds__(512) k_gemm_wide(MatArgs a) {
+  constexpr bool FUSED = EPI == kEpiSwiglu;
+  static_assert(EPI != kEpiArgmax && (MT == 2 || MT == 4), "wide kernel: plain or SwiGLU, 16 or 32 x rows in LDS");
+  constexpr int NQ = FUSED ? 2 : 1;  // weight matrices per tile
+  constexpr int NR = 4 * MT;         // result registers that can hold rows < M
+  extern __shared__ uint4 wide_lds[];
+  const int W = blockDim.x >> 6, NT = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = a.M, N = a.N, K = a.K;
+  const int rb = blockIdx.x, ks = blockIdx.y, S = a.S;
+  const int st0 = ks * a.CRS;                                   // first 256-input step of the slice
+  const int nst = min(a.CRS, (K >> 8) - st0);                   // steps in the slice (even)
+  const int upr = nst << 5;                                     // 16-byte x units per row of the slice
+  const int RS = upr + 1;                                       // LDS row stride in units
+  const int row_lo = rb * a.rq * 32, row_hi = min(N, row_lo + a.rq * 32);
+  const int ntiles = (row_hi - row_lo + 31) >> 5;
+  const int nl = lane & 31, g = lane >> 5;
+
+  // x slice -> LDS: 1 KiB direct-to-LDS loads (each row is whole 64-unit
+  // pieces: the slice is a multiple of 512 inputs), zeros for rows M..8MT-1
+  const float gv0 = load_f32_vmem(a.g0);
+  const float gv1 = FUSED ? load_f32_vmem(a.g1) : 1.0f;
+  {
+    const int ppr = upr >> 6;  // pieces per row
+    const uint4* xg = reinterpret_cast<const uint4*>(a.x) + (size_t)st0 * 32 + lane;
+    for (int j = wv; j < M * ppr; j += W) {
+      const int m = j / ppr, pc = j - m * ppr;
+      __builtin_amdgcn_global_load_lds(xg + (size_t)m * (K >> 3) + pc * 64,
+                                       (__attribute__((address_space(3))) void*)(wide_lds + m * RS + pc * 64),
+                                       16, 0, 0);
+    }
+    for (int u = M * RS + tid; u < 8 * MT * RS; u += NT) wide_lds[u] = make_uint4(0u, 0u, 0u, 0u);
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  __syncthreads();
+  const float ig0 = 1.0f / gv0, ig1 = FUSED ? 1.0f / gv1 : 1.0f;
+  // this lane's A row: lanes 16..31 of a 16-row tile repeat rows 0..15
+  const uint4* xa = wide_lds + (MT == 2 ? (lane & 15) : nl) * RS + g;
+
+  for (int ti = wv; ti < ntiles; ti += W) {
+    const int r0 = row_lo + ti * 32;
+    const int row = min(r0 + nl, row_hi - 1);  // ragged tile: repeat the last row
+    const uint4* qp[NQ];
+    const uint4* sp[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const uint8_t* wq = q ? a.wq1 : a.wq0;
+      const uint8_t* ws = q ? a.ws1 : a.ws0;
+      qp[q] = reinterpret_cast<const uint4*>(wq + (size_t)row * (size_t)(K >> 1)) + 8 * st0 + g;
+      sp[q] = reinterpret_cast<const uint4*>(ws + (size_t)row * (size_t)(K >> 4)) + st0;
+    }
+    // two slots of one step each: 4 x 16 bytes of codes (pieces 2j + g of
+    // the row's 128 bytes) and the step's 16 scale bytes, per matrix
+    uint4 wa[NQ][4], wb2[NQ][4], sa[NQ], sb2[NQ];
+    auto load_step = [&](uint4 (&w)[NQ][4], uint4 (&sc)[NQ], int s) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[q][j] = qp[q][8 * s + 2 * j];
+        sc[q] = sp[q][s];
+      }
+    };
+    f32x16_t acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = f32x16_t{};
+    auto compute_step = [&](uint4 (&w)[NQ][4], uint4 (&sc)[NQ], int s) {
+      // an empty asm that "rewrites" the slot's registers: nothing that reads
+      // them (the lane swaps, the scale conversions) can be scheduled above
+      // it, i.e. above the previous refill, where it would wait for loads
+      // still in flight
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        u32x4_t t0 = __builtin_bit_cast(u32x4_t, w[q][0]), t1 = __builtin_bit_cast(u32x4_t, w[q][1]);
+        u32x4_t t2 = __builtin_bit_cast(u32x4_t, w[q][2]), t3 = __builtin_bit_cast(u32x4_t, w[q][3]);
+        u32x4_t t4 = __builtin_bit_cast(u32x4_t, sc[q]);
+        asm volatile("" : "+v"(t0), "+v"(t1), "+v"(t2), "+v"(t3), "+v"(t4));
+        w[q][0] = __builtin_bit_cast(uint4, t0);
+        w[q][1] = __builtin_bit_cast(uint4, t1);
+        w[q][2] = __builtin_bit_cast(uint4, t2);
+        w[q][3] = __builtin_bit_cast(uint4, t3);
+        sc[q] = __builtin_bit_cast(uint4, t4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t hq[NQ][4];  // half g of blocks 4j .. 4j+3 of the step
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          const auto p0 = __builtin_amdgcn_permlane32_swap(w[q][j].x, w[q][j].y, false, false);
+          const auto p1 = __builtin_amdgcn_permlane32_swap(w[q][j].z, w[q][j].w, false, false);
+          hq[q][0] = p0[0];
+          hq[q][2] = p0[1];
+          hq[q][1] = p1[0];
+          hq[q][3] = p1[1];
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, xa[s * 32 + 8 * j + 2 * b]);
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const uint32_t sw = j == 0 ? sc[q].x : j == 1 ? sc[q].y : j == 2 ? sc[q].z : sc[q].w;
+            float scale;
+            if (b == 0) scale = e4m3_to_f32<0>(sw);
+            else if (b == 1) scale = e4m3_to_f32<1>(sw);
+            else if (b == 2) scale = e4m3_to_f32<2>(sw);
+            else scale = e4m3_to_f32<3>(sw);
+            // the weights times their block scale, exactly (at most 6
+            // significant bits): fp32 products, packed to bf16 without rounding
+            const uint32_t h = hq[q][b];
+            const uint4 bw = make_uint4(scaled_bf16x2<0>(h, scale), scaled_bf16x2<1>(h, scale),
+                                        scaled_bf16x2<2>(h, scale), scaled_bf16x2<3>(h, scale));
+            acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, bw), acc[q], 0, 0, 0);
+          }
+        }
+      }
+    };
+    // (the empty asm statements keep the loads in this order and each refill
+    // ahead of the next step's work: without them the compiler sinks refills
+    // to their first use or reorders the prologue, and the loop then waits
+    // for every load in flight)
+    load_step(wa, sa, 0);
+    asm volatile("" ::: "memory");
+    load_step(wb2, sb2, 1);
+    asm volatile("" ::: "memory");
+    for (int s = 0; s < nst; s += 2) {
+      compute_step(wa, sa, s);
+      load_step(wa, sa, min(s + 2, nst - 1));
+      asm volatile("" ::: "memory");
+      compute_step(wb2, sb2, s + 1);
+      load_step(wb2, sb2, min(s + 3, nst - 1));
+      asm volatile("" ::: "memory");
+    }
+    const int n = r0 + nl;
+    if (n < row_hi) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int m = 8 * (r >> 2) + 4 * g + (r & 3);
+        if (m < M) {
+          const size_t i = (size_t)m * N + n;
+          if (S > 1) {
+            store_coherent(a.part + (size_t)ks * M * N + i, acc[0][r]);
+            if (FUSED) store_coherent(a.part + (size_t)(S + ks) * M * N + i, acc[NQ - 1][r]);
+          } else if (FUSED) {
+            a.y[i] = f32_to_bf16(silu(acc[0][r] * ig0) * (acc[NQ - 1][r] * ig1));
+          } else {
+            a.y[i] = f32_to_bf16(acc[0][r] * ig0);
+          }
+        }
+      }
+    }
+  }
+  if (S > 1) wide_finish<FUSED>(a, rb, row_lo, row_hi - row_lo, ig0, ig1);
+}
+
+// ---------------------------------------------------------------------------
 // Dequantisation to fp32: one thread per dword of codes (8 weights).
 // w = (e2m1 * e4m3) / g: the product is exact in fp32 (at most 6 significant
 // bits), the division is IEEE fp32, so the result is the correctly rounded

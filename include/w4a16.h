@@ -77,10 +77,12 @@ typedef enum {
  *               zero again, so one zero-fill serves any number of calls, of
  *               any shapes, made one after another.  The partial sums after
  *               them need no initialisation.
- *   Wide calls (M > 16) whose single launch would split K very finely run
- *   as two launches on `stream`, over activation rows [0, m1) and [m1, M)
- *   (m1 a multiple of 4), one after the other with the same workspace;
- *   w4a16_workspace_size covers the larger of the two.
+ *   Calls with 17 <= M <= 32 and K a multiple of 512 run as one launch of
+ *   the wide kernel (32 x 32 x 16 MFMA tiles, split-K partials in the
+ *   workspace).  Other wide calls (M > 16) whose single launch would split
+ *   K very finely run as two launches on `stream`, over activation rows
+ *   [0, m1) and [m1, M) (m1 a multiple of 4), one after the other with the
+ *   same workspace; w4a16_workspace_size covers the larger of the two.
  * The operation is the "NVFP4 W4A16" matmul of FlashRT, "Qwen3.6-27B NVFP4
  * on RTX 5090", section 1 (weights in the schema above, bf16 activations).
  * Accuracy contract (this library's own target; the pages state no numeric

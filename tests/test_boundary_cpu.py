@@ -132,6 +132,20 @@ def test_workspace_sizes(lib):
             + max(0, w4.workspace_size(M, 5120, 17408) - 4096)), M
 
 
+def test_wide_kernel_workspace(lib):
+    # 17 <= M <= 32 with K a multiple of 512: one launch of the wide kernel,
+    # whose split-K partials follow the arrival counters.  At 256 CUs the
+    # down projection takes 12 K-slices of 1536 inputs (x: 96 KiB of LDS),
+    # gate/up 3 slices (two partial sets each), the square 10 slices.
+    assert w4.workspace_size(32, 5120, 17408) == 4096 + 12 * 32 * 5120 * 4
+    assert w4.workspace_size(17, 5120, 17408) == 4096 + 12 * 17 * 5120 * 4
+    assert w4.workspace_size_gate_up(32, 17408, 5120) == 4096 + 2 * 3 * 32 * 17408 * 4
+    assert w4.workspace_size(32, 5120, 5120) == 4096 + 10 * 32 * 5120 * 4
+    # K not a multiple of 512 stays on the 4x4x4 kernel (two launches of rows
+    # where its K split would be fine): a different workspace
+    assert w4.workspace_size(32, 5120, 17152) != 4096 + 12 * 32 * 5120 * 4
+
+
 def test_short_workspace_rejected(lib):
     need = w4.workspace_size(8, 5120, 17408)
     assert call_gemm(lib, M=8, N=5120, K=17408, work=P, wbytes=need - 1) == w4.ERR_INVALID_VALUE

@@ -239,6 +239,32 @@ def test_k_column_ring_variant_exact(M, N):
     gemm_exact(M, N, 5120, 2400 + M + N % 89, "mant" if N % 2 else "pow2", ctx="k-column ring")
 
 
+# ---- the wide kernel (9 <= M <= 32, K a multiple of 512) -----------------------
+
+@pytest.mark.parametrize("M", list(range(9, 33)))
+@pytest.mark.parametrize("N,K", [(1003, 1536), (33, 8704)])
+def test_wide_kernel_every_m_exact(M, N, K):
+    """Every M of the wide kernel (17..32; rows M..31 of its tile zero) and of
+    the MFMA kernel below it (9..16): a ragged last tile, and K-slices of
+    several lengths (1536 = three 512-input units, 8704 = seventeen: an
+    uneven last slice)."""
+    gemm_exact(M, N, K, 2500 + M + K % 97, "mant" if M % 2 else "pow2", ctx="wide")
+
+
+@pytest.mark.parametrize("M,N", [(17, 1), (18, 31), (17, 32), (32, 33), (24, 5121), (32, 17409)])
+def test_wide_kernel_ragged_n_exact(M, N):
+    """Row counts around the 32-row tile and the row block of W tiles."""
+    gemm_exact(M, N, 5120, 2550 + M + N % 89, ctx="wide ragged")
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 777, 1024), (20, 17408, 5120), (17, 1029, 2048), (32, 17408, 5120),
+                                   (29, 65, 512)])
+def test_wide_kernel_fused_exact(M, N, K):
+    """Gate and up tiles side by side on the same x reads; split-K partials of
+    both (two sets per slice) added by the row block's last workgroup."""
+    fused_exact(M, N, K, 2600 + M, ctx="wide fused")
+
+
 # ---- one-hot sweep: every 32-input chunk position of K = 5120 -----------------
 
 @pytest.mark.parametrize("M", [2, 8, 16])

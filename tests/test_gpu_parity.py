@@ -223,10 +223,11 @@ def test_nan_scale_propagates_to_its_row_only():
         assert not np.isnan(np.delete(y, 17, axis=1)).any()
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 7, 8])
+@pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 16, 32])
 def test_uniform_random_bytes_at_k5120(M):
-    """The K = 5120 kernels (whole-row for M <= 2, K-column for 3 <= M <= 8) on
-    every code byte and random finite scales of both signs."""
+    """The K = 5120 kernels (whole-row for M <= 2, K-column for 3 <= M <= 8,
+    MFMA for 9 <= M <= 16, wide for 17 <= M <= 32) on every code byte and
+    random finite scales of both signs."""
     N, K = 300, 5120
     wq = synth.random_bytes(21, (N, K // 2))
     ws = synth.random_bytes(22, (N, K // 16)) & np.uint8(0x77)
@@ -234,10 +235,12 @@ def test_uniform_random_bytes_at_k5120(M):
     check_gemm(wq, ws, np.float32(1234.5), synth.activations(24 + M, M, K), M, N, K, "random bytes K=5120")
 
 
-@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("M", [1, 4, 8, 16, 17, 32])
 def test_nan_scale_propagates_to_its_row_only_at_k5120(M):
     """A NaN block scale (E4M3 0x7F) in one row reaches that row's outputs
-    only, through the K = 5120 kernels' lane, block and wave reductions."""
+    only, through the K = 5120 kernels' lane, block and wave reductions (the
+    wide kernel: one MFMA result column, its K-slice partial and the
+    split-K sum)."""
     N, K = 300, 5120
     wq, ws, g = weights(25, N, K)
     ws = ws.copy()
@@ -314,8 +317,8 @@ def test_run_to_run_bitwise(M, N, K):
     assert all(torch.equal(ys[0], t) for t in ys[1:])
 
 
-@pytest.mark.parametrize("family,Ms", [("valu", (1, 2)), ("mfma", (3, 4, 5, 8)),
-                                       ("mfma one quad per task", (17, 21, 24))])
+@pytest.mark.parametrize("family,Ms", [("valu", (1, 2)), ("k-column", (3, 4, 5, 8)),
+                                       ("wide", (17, 21, 24, 32))])
 def test_rows_do_not_depend_on_m_within_a_kernel_family(family, Ms):
     N, K = 300, 5120
     wq, ws, g = weights(16, N, K)
