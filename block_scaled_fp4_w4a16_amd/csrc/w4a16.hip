@@ -280,72 +280,103 @@ struct WideEntry {
   const void* fn;
 };
 #define W4A16_WE(MT, F) {MT, F, reinterpret_cast<const void*>(&k_gemm_wide<MT, F>)},
-const WideEntry kWideKernels[] = {W4A16_WE(4, kEpiPlain) W4A16_WE(4, kEpiSwiglu)};
+const WideEntry kWideKernels[] = {W4A16_WE(2, kEpiPlain) W4A16_WE(4, kEpiPlain) W4A16_WE(4, kEpiSwiglu)
+#ifdef W4A16_TUNING
+                                  W4A16_WE(2, kEpiSwiglu)
+#endif
+};
 #undef W4A16_WE
 const void* find_wide_kernel(int mt, int epi) {
   for (const WideEntry& e : kWideKernels)
     if (e.mt == mt && e.epi == epi) return e.fn;
   return nullptr;
 }
-// From 17 rows on (measured on MI355X by HIP-graph replay, M = 9 / 16 / 24 /
-// 32, wide kernel against the 4x4x4 MFMA kernel: down 5120 x 17408 22.5 /
-// 23.2 / 26.6 / 27.4 us against 19.9 / 24.0 / 36.1 / 47.8; gate/up 2 x 17408
-// x 5120 43.2 / 45.0 / 48.4 / 51.4 against 28.1 / 42.1 / 56.3 / 83.1; the
-// square 5120^2 14.1 / 14.7 / 17.6 / 18.0 against 9.1 / 13.0 / 16.0 / 23.3).
-// Below that the wide kernel's fixed costs (x staging, partial sums and their
-// finish) outweigh what it saves.
-constexpr int kWideMinM = 17;
+// From 16 rows on for plain calls, 17 for gate/up (measured on MI355X by
+// HIP-graph replay, M = 16 / 17 / 24 / 32, wide kernel against the 4x4x4 MFMA
+// kernel: down 5120 x 17408 19.5 / 24.7 / 26.6 / 27.3 us against 23.5 / 30.5
+// / 36.1 / 46.8; the square 5120^2 10.9 / 12.5 / 12.8 / 13.1 against 12.9 /
+// 14.3 / 16.0 / 23.1; gate/up 2 x 17408 x 5120 41.5 / 41.3 / 42.5 / 44.7
+// against 41.5 / 48.8 / 55.3 / 82.7).  Below that the wide kernel's fixed
+// costs (x staging, partial sums and their finish) outweigh what it saves
+// (M = 9, first plans: down 22.5 against 19.9 us, the square 14.1 against 9.1).
+constexpr int kWideMinM = 16, kWideMinMFused = 17;
 // LDS bytes of k_gemm_wide<mt, ...> for a K-slice of `steps` steps of 256
 // inputs: 8 * mt rows of steps * 32 units of 16 bytes, plus one unit per row
 size_t wide_lds(int mt, int steps) { return (size_t)8 * mt * ((size_t)steps * 32 + 1) * 16; }
 
-// Plan for the wide kernel, or false if it does not apply.  Row blocks of 8
-// tiles (one per wave: two waves per SIMD, so that one runs while the other
-// waits for memory); K-slices of u x 512 inputs (the slice's x must fit in
-// LDS).  Among every u, the plan with the least estimated time: the busiest
-// SIMD's tile work (tiles x 512 inputs, ~1.2 us each) plus the split-K
-// partials written and read back (at ~4 TB/s); ties go to fewer slices, then
-// to fewer rounds of workgroups.
+#ifdef W4A16_TUNING
+// Tuning builds only: force the wide kernel's waves, slice length (units of
+// 512 inputs) and smallest M (0 = the planner's choice).
+int g_wide_W = 0, g_wide_u = 0, g_wide_minm = 0;
+bool g_wide_any(int W, int u) { return g_wide_W == W && g_wide_u == u; }
+#else
+constexpr bool g_wide_any(int, int) { return false; }
+#endif
+// Plan for the wide kernel, or false if it does not apply.  Row blocks of W
+// tiles (one per wave), W = 4 or 8; K-slices of u x 512 inputs (the slice's x
+// must fit in LDS).  Rule, from a sweep of W and u on MI355X (HIP-graph
+// replay; 5120 x 17408, 2 x 17408 x 5120 and 5120^2 at M = 16, 24, 32): the
+// most workgroups that still run in one round, at most one per CU for a
+// plain call (a second one on a CU doubles its SIMDs' work), up to 2.2 per CU
+// for gate/up (whose per-workgroup work is twice as long and tolerates a
+// partial second round better than an idle CU); ties go to fewer K-slices
+// (fewer partial sums), then to fewer waves.  Chosen and measured: the down
+// projection 8 waves x 12 slices (27.3 us at M = 32; 6 slices: 29.9), 4 x 6
+// at M = 16 (19.4; 8 x 12: 23.2); the square 4 x 5 (13.0 at M = 32, 10.8 at
+// M = 16; 8 x 10: 18.0 / 14.7); gate/up 4 x 4 at M = 32 (44.9; 8 x 3: 51.8).
 bool plan_wide(int M, int N, int K, int epi, Plan& pl) {
-  if (M < kWideMinM || M > 32 || epi == kEpiArgmax || K % 512 != 0) return false;
+  const bool fused = epi == kEpiSwiglu;
+  int min_m = fused ? kWideMinMFused : kWideMinM;
 #ifdef W4A16_TUNING
   if (g_override.enable) return false;
+  if (g_wide_minm > 0) min_m = g_wide_minm;
 #endif
-  const int mt = 4;
-  const bool fused = epi == kEpiSwiglu;
+  if (M < min_m || M > 32 || epi == kEpiArgmax || K % 512 != 0) return false;
+  const int mt = M <= 16 ? 2 : 4;
   if (!find_wide_kernel(mt, epi)) return false;
   const int cus = cu_count();
   const long long T = ((long long)N + 31) / 32;
   const int units = K / 512;
-  const double unit_us = 1.2 * (fused ? 2 : 1);
-  double best = 1e30;
+  const long long cap = fused ? (long long)cus * 22 / 10 : cus;
+  long long best_wgs = -1;
   int bW = 0, bu = 0, bS = 0;
-  long long bnrb = 0, brounds = 0;
-  for (int W = 8; W <= 8; ++W) {  // two waves per SIMD (one hides the other's waits)
+  long long bnrb = 0;
+  int Wlo = 4, Whi = 8;
+#ifdef W4A16_TUNING
+  if (g_wide_W > 0) Wlo = Whi = g_wide_W;
+#endif
+  for (int W = Wlo; W <= Whi; W += 4) {
     const long long nrb = (T + W - 1) / W;
     for (int u = 1; u <= units; ++u) {
+#ifdef W4A16_TUNING
+      if (g_wide_u > 0 && u != g_wide_u) continue;
+#endif
       const size_t lds = wide_lds(mt, 2 * u);
       if (lds > kMaxLds) break;
       const int S = (units + u - 1) / u;
       if (S > 1 && nrb > kMaxSplitRowBlocks) continue;
-      long long per_cu = (long long)(kMaxLds / lds);
-      const long long wave_cap = W <= 4 ? 2 : 1;  // two waves per SIMD
-      if (per_cu > wave_cap) per_cu = wave_cap;
       const long long wgs = nrb * S;
-      const long long wg_per_cu = (wgs + cus - 1) / cus;
-      const long long rounds = (wgs + cus * per_cu - 1) / (cus * per_cu);
-      const double load = (double)((wg_per_cu * W + 3) / 4) * u;
-      const double part = S > 1 ? 2.0 * S * M * (double)N * 4 * (fused ? 2 : 1) : 0.0;
-      const double t = load * unit_us + part / 4e6;
-      if (t < best - 1e-9 || (t < best + 1e-9 && (S < bS || (S == bS && rounds < brounds)))) {
-        best = t;
+      const bool fits = wgs <= cap || (g_wide_any(W, u));
+      if (!fits) continue;
+      if (wgs > best_wgs || (wgs == best_wgs && (S < bS || (S == bS && W < bW)))) {
+        best_wgs = wgs;
         bW = W;
         bu = u;
         bS = S;
         bnrb = nrb;
-        brounds = rounds;
       }
     }
+  }
+  // nothing runs in one round (very wide rows): the fewest workgroups
+  if (bW == 0) {
+    for (int u = units; u >= 1; --u)
+      if (wide_lds(mt, 2 * u) <= kMaxLds && ((T + 7) / 8 <= kMaxSplitRowBlocks || (units + u - 1) / u == 1)) {
+        bW = 8;
+        bu = u;
+        bS = (units + u - 1) / u;
+        bnrb = (T + 7) / 8;
+        break;
+      }
   }
   if (bW == 0) return false;
   pl = Plan{};
@@ -1205,6 +1236,11 @@ __attribute__((visibility("default"))) void w4a16_tuning_plan(int M, int N, int 
   const long long v[12] = {pl.mfma, pl.lr, pl.D, pl.W, pl.LB, pl.nrb, pl.S,
                            pl.rq, pl.rr, pl.kmax, (long long)pl.lds, (long long)pl.ws};
   for (int i = 0; i < 12; ++i) out[i] = v[i];
+}
+__attribute__((visibility("default"))) void w4a16_tuning_wide(int W, int u, int min_m) {
+  g_wide_W = W;
+  g_wide_u = u;
+  g_wide_minm = min_m;
 }
 // Tuning builds only: the wide kernel's part of the plan, as 7 ints
 // {wide_mt, wide_steps, W, nrb, S, lds, ws} (wide_mt = 0: another kernel).

@@ -226,7 +226,7 @@ def test_nan_scale_propagates_to_its_row_only():
 @pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 16, 32])
 def test_uniform_random_bytes_at_k5120(M):
     """The K = 5120 kernels (whole-row for M <= 2, K-column for 3 <= M <= 8,
-    MFMA for 9 <= M <= 16, wide for 17 <= M <= 32) on every code byte and
+    MFMA for 9 <= M <= 15, wide for 16 <= M <= 32) on every code byte and
     random finite scales of both signs."""
     N, K = 300, 5120
     wq = synth.random_bytes(21, (N, K // 2))
