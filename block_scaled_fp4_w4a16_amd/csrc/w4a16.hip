@@ -291,15 +291,17 @@ const void* find_wide_kernel(int mt, int epi) {
     if (e.mt == mt && e.epi == epi) return e.fn;
   return nullptr;
 }
-// From 16 rows on for plain calls, 17 for gate/up (measured on MI355X by
-// HIP-graph replay, M = 16 / 17 / 24 / 32, wide kernel against the 4x4x4 MFMA
-// kernel: down 5120 x 17408 19.5 / 24.7 / 26.6 / 27.3 us against 23.5 / 30.5
-// / 36.1 / 46.8; the square 5120^2 10.9 / 12.5 / 12.8 / 13.1 against 12.9 /
-// 14.3 / 16.0 / 23.1; gate/up 2 x 17408 x 5120 41.5 / 41.3 / 42.5 / 44.7
-// against 41.5 / 48.8 / 55.3 / 82.7).  Below that the wide kernel's fixed
-// costs (x staging, partial sums and their finish) outweigh what it saves
-// (M = 9, first plans: down 22.5 against 19.9 us, the square 14.1 against 9.1).
-constexpr int kWideMinM = 16, kWideMinMFused = 17;
+// From 13 rows on for plain calls, 17 for gate/up (measured on MI355X by
+// HIP-graph replay, wide kernel against the 4x4x4 MFMA kernel: the square
+// 5120^2 at M = 12 / 13 / 16 / 24 / 32 10.7 / 10.7 / 10.8 / 12.8 / 13.1 us
+// against 9.5 / 12.5 / 13.0 / 16.0 / 23.1 (the 4x4x4 kernel takes a fourth
+// row pass from M = 13); down 5120 x 17408 at M = 9 / 13 / 16 / 24 / 32 19.1
+// / 19.3 / 19.4 / 26.6 / 27.3 against 19.5 / 22.9 / 23.8 / 36.1 / 46.8;
+// gate/up 2 x 17408 x 5120 at M = 13 / 16 / 17 / 24 / 32 43.8 / 44.8 / 41.3 /
+// 42.5 / 44.7 against 40.2 / 41.7 / 48.8 / 55.3 / 82.7).  Below that the wide
+// kernel's fixed costs (x staging, partial sums and their finish) outweigh
+// what it saves.
+constexpr int kWideMinM = 13, kWideMinMFused = 17;
 // LDS bytes of k_gemm_wide<mt, ...> for a K-slice of `steps` steps of 256
 // inputs: 8 * mt rows of steps * 32 units of 16 bytes, plus one unit per row
 size_t wide_lds(int mt, int steps) { return (size_t)8 * mt * ((size_t)steps * 32 + 1) * 16; }

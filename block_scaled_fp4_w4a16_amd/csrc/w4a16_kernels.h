@@ -1809,7 +1809,7 @@ __global__ void __launch_bounds__(LB) k_gemm_mfma(MatArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide kernel, 16 <= M <= 32: one 32 x 32 x 16 bf16 MFMA per 16-input scale
+// Wide kernel, 13 <= M <= 32: one 32 x 32 x 16 bf16 MFMA per 16-input scale
 // block, accumulating over the whole K-slice.  An E2M1 value times an E4M3
 // scale has at most 6 significant bits, so each weight times its block scale
 // is exact in bf16: the weights enter the MFMA already scaled (fp32 products

@@ -77,7 +77,7 @@ typedef enum {
  *               zero again, so one zero-fill serves any number of calls, of
  *               any shapes, made one after another.  The partial sums after
  *               them need no initialisation.
- *   Calls with 16 <= M <= 32 (gate/up: 17) and K a multiple of 512 run as one launch of
+ *   Calls with 13 <= M <= 32 (gate/up: 17) and K a multiple of 512 run as one launch of
  *   the wide kernel (32 x 32 x 16 MFMA tiles, split-K partials in the
  *   workspace).  Other wide calls (M > 16) whose single launch would split
  *   K very finely run as two launches on `stream`, over activation rows

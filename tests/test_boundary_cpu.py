@@ -133,14 +133,15 @@ def test_workspace_sizes(lib):
 
 
 def test_wide_kernel_workspace(lib):
-    # 16 <= M <= 32 (gate/up: 17) with K a multiple of 512: one launch of the
+    # 13 <= M <= 32 (gate/up: 17) with K a multiple of 512: one launch of the
     # wide kernel, whose split-K partials follow the arrival counters.  At 256
     # CUs the down projection takes 12 K-slices of 1536 inputs at M >= 17
-    # (x: 96 KiB of LDS) and 6 of 3072 at M = 16, gate/up 4 slices (two
+    # (x: 96 KiB of LDS) and 6 of 3072 at M <= 16, gate/up 4 slices (two
     # partial sets each), the square 5 slices.
     assert w4.workspace_size(32, 5120, 17408) == 4096 + 12 * 32 * 5120 * 4
     assert w4.workspace_size(17, 5120, 17408) == 4096 + 12 * 17 * 5120 * 4
     assert w4.workspace_size(16, 5120, 17408) == 4096 + 6 * 16 * 5120 * 4
+    assert w4.workspace_size(13, 5120, 17408) == 4096 + 6 * 13 * 5120 * 4
     assert w4.workspace_size_gate_up(32, 17408, 5120) == 4096 + 2 * 4 * 32 * 17408 * 4
     assert w4.workspace_size(32, 5120, 5120) == 4096 + 5 * 32 * 5120 * 4
     # K not a multiple of 512 stays on the 4x4x4 kernel (two launches of rows

@@ -244,8 +244,8 @@ def test_k_column_ring_variant_exact(M, N):
 @pytest.mark.parametrize("M", list(range(9, 33)))
 @pytest.mark.parametrize("N,K", [(1003, 1536), (33, 8704)])
 def test_wide_kernel_every_m_exact(M, N, K):
-    """Every M of the wide kernel (16..32; x rows M..8*MT-1 in LDS zero) and
-    of the MFMA kernel below it (9..15): a ragged last tile, and K-slices of
+    """Every M of the wide kernel (13..32; x rows M..8*MT-1 in LDS zero) and
+    of the MFMA kernel below it (9..12): a ragged last tile, and K-slices of
     several lengths (1536 = three 512-input units, 8704 = seventeen: an
     uneven last slice)."""
     gemm_exact(M, N, K, 2500 + M + K % 97, "mant" if M % 2 else "pow2", ctx="wide")

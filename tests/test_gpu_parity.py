@@ -226,7 +226,7 @@ def test_nan_scale_propagates_to_its_row_only():
 @pytest.mark.parametrize("M", [1, 2, 3, 7, 8, 16, 32])
 def test_uniform_random_bytes_at_k5120(M):
     """The K = 5120 kernels (whole-row for M <= 2, K-column for 3 <= M <= 8,
-    MFMA for 9 <= M <= 15, wide for 16 <= M <= 32) on every code byte and
+    MFMA for 9 <= M <= 12, wide for 13 <= M <= 32) on every code byte and
     random finite scales of both signs."""
     N, K = 300, 5120
     wq = synth.random_bytes(21, (N, K // 2))
@@ -318,7 +318,8 @@ def test_run_to_run_bitwise(M, N, K):
 
 
 @pytest.mark.parametrize("family,Ms", [("valu", (1, 2)), ("k-column", (3, 4, 5, 8)),
-                                       ("wide", (17, 21, 24, 32))])
+                                       ("wide", (17, 21, 24, 32)),
+                                       ("wide, 16 rows of x", (13, 14, 16))])
 def test_rows_do_not_depend_on_m_within_a_kernel_family(family, Ms):
     N, K = 300, 5120
     wq, ws, g = weights(16, N, K)
