@@ -369,7 +369,8 @@ def test_split_k_workspace_reused_by_many_calls():
     # back on one workspace, each checked against the oracle, twice
     work = torch.zeros((1 << 22,), dtype=torch.uint8, device="cuda")
     cases = [(8, 640, 17408, False), (5, 1003, 17408, False), (16, 96, 33024, False),
-             (7, 5120, 17408, False), (6, 200, 17408, True), (2, 640, 17408, False)]
+             (7, 5120, 17408, False), (6, 200, 17408, True), (2, 640, 17408, False),
+             (32, 1003, 17408, False), (20, 777, 5120, True), (13, 640, 5120, False)]
     for i, (M, N, K, fused) in enumerate(cases):
         need = (w4.workspace_size_gate_up if fused else w4.workspace_size)(M, N, K)
         assert need <= work.numel()
@@ -393,7 +394,9 @@ def test_split_k_workspace_reused_by_many_calls():
 
 
 def test_graph_capture_replays_match_eager():
-    cases = [(1, 5120, 5120), (7, 5120, 17408)]
+    # M = 16 and 32 of the down projection: the wide kernel (split-K partials,
+    # arrival counters reset by each call's finishing workgroup)
+    cases = [(1, 5120, 5120), (7, 5120, 17408), (16, 5120, 17408), (32, 5120, 17408)]
     for M, N, K in cases:
         wq, ws, g = weights(22, N, K)
         dwq, dws, dg = d_u8(wq), d_u8(ws), d_g(g)
