@@ -13,11 +13,11 @@ The same line carries the metric's two operating points (M = 1 decode and
 M = 7, a verify block of 6 drafts + 1) on the configurations that define
 them: the square projection at M = 7, the fused gate/up + SwiGLU (K = 5120,
 2 x N = 17408, 32 layer copies) and the down projection (K = 17408,
-N = 5120, 32 copies), each at M = 1 and 7 with median and minimum over 5
+N = 5120, 32 copies), each at M = 1, 7 and 32 with median and minimum over 5
 timed windows; the oracle timed on the host (one thread and all cores); an
 achievable-read calibration; and the full-tower decode sweep (64 layers of
 gate/up, down and q/k/v/o plus the 5120 -> 248320 head, M = 1 and 7; skip it
-with --no-tower).  `--extra` adds the down projection at M = 2, 4, 8, 16, 32
+with --no-tower).  `--extra` adds the down projection at M = 2, 4, 8, 16
 and the MLP block.
 
 Inputs are resident in HBM before any timed region starts.
@@ -331,8 +331,9 @@ def square_m_fns(sq, M, dev):
 
 
 def bench_configs(dev, stream, sq, extra=False):
-    """Square M = 7; gate/up + SwiGLU M = 1, 7; down M = 1, 7 (with --extra
-    also down M = 2, 4, 8, 16, 32 and the MLP block)."""
+    """Square M = 7; gate/up + SwiGLU M = 1, 7, 32; down M = 1, 7, 32 (with
+    --extra also down M = 2, 4, 8, 16 and the MLP block).  M = 32, a wide
+    verify or prefill block, runs the 32 x 32 x 16 MFMA kernel."""
     import torch
     import block_scaled_fp4_w4a16_amd as w4
     import synth
@@ -342,13 +343,13 @@ def bench_configs(dev, stream, sq, extra=False):
     log(f"[bench] square M=7: {out['square_M7']['us_per_call']} us/call, {out['square_M7']['gbs']} GB/s")
 
     Gs, Us = gate_up_weights(dev)
-    for M in (1, 7):
+    for M in (1, 7, 32):
         fns, b = gate_up_fns(Gs, Us, M, dev)
         out[f"gate_up_M{M}"] = time_config(fns, stream, b)
         log(f"[bench] gate/up M={M}: {out[f'gate_up_M{M}']['us_per_call']} us/call, {out[f'gate_up_M{M}']['gbs']} GB/s")
 
     Ds = down_weights(dev)
-    for M in ((1, 2, 4, 7, 8, 16, 32) if extra else (1, 7)):
+    for M in ((1, 2, 4, 7, 8, 16, 32) if extra else (1, 7, 32)):
         fns, b = down_fns(Ds, M, dev)
         out[f"down_M{M}"] = time_config(fns, stream, b)
         log(f"[bench] down M={M}: {out[f'down_M{M}']['us_per_call']} us/call, {out[f'down_M{M}']['gbs']} GB/s")
